@@ -1,0 +1,179 @@
+/*
+ * mla.h -- C ABI of libmla.so: MLA absorbed decode on AMD MI355X (gfx950).
+ *
+ * Multi-head Latent Attention caches, per token and layer, only a joint KV
+ * latent c (d_c = 512) and one decoupled RoPE key k^R (d_R = 64) that every
+ * head shares (PaperTrace "02 · DeepSeek-V2 analysis", sections 1.2-1.3:
+ * 576 elements per token per layer). At decode time each head's content
+ * query is absorbed into the latent space through W^UK (section 1.2 and
+ * section 6), scores are q_lat.c + q_rope.k^R scaled by 1/sqrt(d_h + d_R)
+ * (eq. 18), softmax runs over the cached tokens, each head aggregates
+ * latents u = sum_s a_s c_s, and only then applies its own W^UV (section 6.1).
+ *
+ * Conventions for every entry point:
+ *  - Tensor pointers are DEVICE pointers, owned by the caller, contiguous in
+ *    the layout stated (row-major, last index fastest). The library never
+ *    allocates, frees or keeps a pointer after the call returns.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = default stream) and
+ *    is stream-ordered; the library never synchronizes.
+ *  - Arguments are checked on the host before anything is launched; a bad
+ *    argument returns an error status and launches nothing. A failed launch
+ *    returns MLA_ERR_LAUNCH. No C++ exception crosses this ABI.
+ *  - Device-side data the host cannot see (sequence lengths, block-table
+ *    entries) is range-checked in the kernel: a sequence whose length or
+ *    page ids are out of range gets NaN outputs instead of a memory fault.
+ *  - Results are deterministic: no atomics, fixed reduction order; the
+ *    order depends on logical token indices only, never on physical pages.
+ *  - There is no global mutable state; calls are thread-safe.
+ *
+ * dtypes: MLA_F32 = IEEE binary32, MLA_BF16 = bfloat16, MLA_FP8_E4M3 = OCP
+ * E4M3FN (bias 7, max 448, no infinities) with one fp32 scale per token.
+ */
+#ifndef MLA_H
+#define MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_ABI_VERSION 1
+#define MLA_PAGE_SIZE 64
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_NULL = 1,        /* a required pointer is NULL */
+  MLA_ERR_SHAPE = 2,       /* a size is out of range or inconsistent */
+  MLA_ERR_DTYPE = 3,       /* dtype combination not supported */
+  MLA_ERR_UNSUPPORTED = 4, /* shape outside what the kernels implement */
+  MLA_ERR_WORKSPACE = 5,   /* workspace missing or too small */
+  MLA_ERR_LAUNCH = 6       /* the HIP launch failed */
+} mla_status;
+
+typedef enum { MLA_F32 = 0, MLA_BF16 = 1, MLA_FP8_E4M3 = 2 } mla_dtype;
+
+/* Human-readable name of a status code (static string; never NULL). */
+const char* mla_status_str(int status);
+
+/* MLA_ABI_VERSION of the built library. */
+int mla_abi_version(void);
+
+/*
+ * mla_absorb_q -- absorb W^UK into the content query.
+ *   q_lat[n][h][:] = W_UK[h]^T q_nope[n][h][:]
+ * i.e. q^T (W^UK c) = (W^UK^T q)^T c (V2 analysis page, section 1.2 and the
+ * first absorption condition of section 6: a fixed linear map moved to the
+ * query side).
+ *   q_nope : [n_tok][H][d_h]  dtype q_dt (F32 or BF16)
+ *   w_uk   : [H][d_h][d_c]    dtype q_dt (head h's up-projection, d_h x d_c)
+ *   q_lat  : [n_tok][H][d_c]  dtype out_dt (F32, or BF16 when q_dt is BF16)
+ * Supported: d_h = 128, d_c = 512, n_tok >= 0 (0 launches nothing), H >= 1.
+ * Accumulation is fp32; F32 inputs use fp32 FMA end to end.
+ */
+int mla_absorb_q(const void* q_nope, const void* w_uk, void* q_lat,
+                 int q_dt, int out_dt, int n_tok, int H, int d_h, int d_c,
+                 void* stream);
+
+/*
+ * mla_rope -- rotary position embedding of the decoupled rope query or key.
+ * Coordinate pairs (2i, 2i+1) are rotated at position n (CSDN "DeepSeek-V3
+ * structure and engineering", section 2(3)); the rope part is decoupled from
+ * the absorbed content part (V2 analysis page, section 1.3, eq. 14-15):
+ *   a = pos[n] * base^(-2i/d_r)           (angle in fp64)
+ *   y[2i]   = x[2i] cos a - x[2i+1] sin a
+ *   y[2i+1] = x[2i] sin a + x[2i+1] cos a
+ *   x_in, x_out : [n_tok][n_heads][d_r], dtype dt (F32 or BF16); may alias
+ *                 exactly (in place)
+ *   pos         : int32 [n_tok], positions >= 0
+ * Supported: d_r even, 2 <= d_r <= 256; n_tok >= 0.
+ */
+int mla_rope(const void* x_in, void* x_out, int dt, const int32_t* pos,
+             int n_tok, int n_heads, int d_r, double base, void* stream);
+
+/*
+ * Arguments of the paged absorbed-decode kernel.
+ *
+ * Paged cache: token s of sequence b lives in page block_table[b][s / 64],
+ * slot s % 64, of two pools that hold the 512 latent and the 64 rotated rope
+ * elements of each token (the 576-element cache of the V2 analysis page,
+ * section 1.3; the key is cached already rotated, section 6).
+ *
+ * Query rows: row (b, t, h) is query token t (0 <= t < T) of sequence b and
+ * head h; it sits at position L_b - T + t and attends to tokens
+ * s <= L_b - T + t (the T new tokens are already in the cache; T = 2 gives
+ * the causal mask between two speculative tokens).
+ */
+typedef struct mla_decode_args {
+  int32_t B, T, H;          /* batch, query tokens per sequence (1 or 2), heads */
+  int32_t d_c, d_r;         /* latent and rope widths: must be 512 and 64 */
+  int32_t page_size;        /* must be MLA_PAGE_SIZE */
+  int32_t n_pages;          /* pages in each pool (bound for block-table ids) */
+  int32_t max_pages_per_seq;/* row length of block_table */
+  int32_t max_seq_len;      /* host upper bound on seq_lens[b] */
+  int32_t q_dt;             /* dtype of q_lat and q_rope: F32 or BF16 */
+  int32_t ckv_dt;           /* latent pool: F32, BF16 or FP8_E4M3 */
+  int32_t kr_dt;            /* rope pool: F32 (iff ckv_dt is F32) or BF16 */
+  int32_t out_dt;           /* u: F32 or BF16 */
+  int32_t split_tokens;     /* 0 = auto; else a multiple of 64: split k covers
+                               tokens [k*split_tokens, (k+1)*split_tokens) */
+  int64_t total_tokens;     /* host hint: sum of seq_lens (0 = unknown) */
+  float softmax_scale;      /* 1/sqrt(d_h + d_r) for DeepSeek-V2 (eq. 18) */
+  int32_t reserved0;        /* must be 0 */
+  const void* q_lat;        /* [B][T][H][d_c] absorbed queries (mla_absorb_q) */
+  const void* q_rope;       /* [B][T][H][d_r] rotated rope queries (mla_rope) */
+  const void* ckv;          /* [n_pages][64][d_c] latent pool */
+  const void* kr;           /* [n_pages][64][d_r] rotated rope-key pool */
+  const float* ckv_scale;   /* [n_pages][64] fp32 per-token scale iff ckv_dt is
+                               FP8_E4M3 (value = code * scale), else NULL */
+  const int32_t* block_table;/* [B][max_pages_per_seq] page ids */
+  const int32_t* seq_lens;  /* [B] cached length L_b incl. the T new tokens;
+                               T <= L_b <= max_seq_len */
+  void* out;                /* [B][T][H][d_c] u = sum_s a_s c_s, dtype out_dt */
+  float* lse;               /* [B][T][H] natural-log sum of exp(scores), or NULL */
+  void* workspace;          /* device scratch of workspace_bytes (split partials) */
+  size_t workspace_bytes;
+} mla_decode_args;
+
+/*
+ * mla_decode_plan -- host-only: the split size, split count and workspace
+ * bytes mla_decode_paged will use for these arguments (pointers may be NULL).
+ * With more than one split, each (sequence, split, 64-row group) produces
+ * fp32 partials (m, l, U) merged by a log-sum-exp combine kernel.
+ */
+int mla_decode_plan(const mla_decode_args* args, int* split_tokens, int* n_split,
+                    size_t* workspace_bytes);
+
+/*
+ * mla_decode_paged -- absorbed MLA decode over the paged cache (V2 analysis
+ * page, sections 1.2-1.3 and 6.1):
+ *   z_s  = (q_lat . c_s + q_rope . k^R_s) * softmax_scale
+ *   a_s  = softmax over the visible s
+ *   u    = sum_s a_s c_s            (latent-space aggregate, W^UV not applied)
+ *   lse  = ln sum_s exp(z_s)
+ * F32 caches run an fp32 kernel; BF16 caches run bf16 MFMA with fp32 softmax
+ * and accumulation; FP8_E4M3 latents run fp8 MFMA for the latent scores
+ * (q_lat quantized per row after absorption) and bf16 MFMA for rope and
+ * aggregation, scales applied in fp32.
+ */
+int mla_decode_paged(const mla_decode_args* args, void* stream);
+
+/*
+ * mla_out_proj -- each head's value up-projection applied after aggregation
+ * (V2 analysis page, section 6.1: per-head aggregation first, then the head's
+ * own matrix; the heads' matrices cannot be summed):
+ *   o[n][h][:] = W_UV[h] u[n][h][:]
+ *   u    : [n_tok][H][d_c]  dtype u_dt (F32 or BF16)
+ *   w_uv : [H][d_h][d_c]    dtype w_dt (F32 or BF16; F32 requires u_dt F32)
+ *   o    : [n_tok][H][d_h]  dtype o_dt (F32 or BF16)
+ * Supported: d_h = 128, d_c = 512. fp32 accumulation.
+ */
+int mla_out_proj(const void* u, const void* w_uv, void* o, int u_dt, int w_dt,
+                 int o_dt, int n_tok, int H, int d_h, int d_c, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H */

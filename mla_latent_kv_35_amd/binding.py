@@ -1,0 +1,291 @@
+"""Python binding of libmla.so (ctypes). Argument marshalling only.
+
+Every step of the decode path runs in the HIP kernels behind the C ABI
+declared in include/mla.h; this module allocates outputs and workspaces as
+torch device tensors, passes raw pointers and the current HIP stream, and
+turns non-zero status codes into exceptions. Importing it fails loudly when
+the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmla.so")
+
+MLA_F32, MLA_BF16, MLA_FP8_E4M3 = 0, 1, 2
+PAGE_SIZE = 64
+_DT = {"f32": MLA_F32, "bf16": MLA_BF16, "fp8": MLA_FP8_E4M3}
+_TORCH_DT = {MLA_F32: torch.float32, MLA_BF16: torch.bfloat16, MLA_FP8_E4M3: torch.uint8}
+
+
+class MlaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {_lib.mla_status_str(status).decode()} (status {status})")
+        self.status = status
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m mla_latent_kv_35_amd.build` "
+                      "(or __graft_entry__.build()); there is no fallback path")
+_lib = ctypes.CDLL(LIB_PATH)
+
+
+class DecodeArgs(ctypes.Structure):
+    """Mirror of mla_decode_args (include/mla.h)."""
+    _fields_ = [
+        ("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
+        ("d_c", ctypes.c_int32), ("d_r", ctypes.c_int32),
+        ("page_size", ctypes.c_int32), ("n_pages", ctypes.c_int32),
+        ("max_pages_per_seq", ctypes.c_int32), ("max_seq_len", ctypes.c_int32),
+        ("q_dt", ctypes.c_int32), ("ckv_dt", ctypes.c_int32), ("kr_dt", ctypes.c_int32),
+        ("out_dt", ctypes.c_int32), ("split_tokens", ctypes.c_int32),
+        ("total_tokens", ctypes.c_int64),
+        ("softmax_scale", ctypes.c_float), ("reserved0", ctypes.c_int32),
+        ("q_lat", ctypes.c_void_p), ("q_rope", ctypes.c_void_p),
+        ("ckv", ctypes.c_void_p), ("kr", ctypes.c_void_p), ("ckv_scale", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
+        ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+_vp, _i, _d = ctypes.c_void_p, ctypes.c_int, ctypes.c_double
+_lib.mla_status_str.restype = ctypes.c_char_p
+_lib.mla_status_str.argtypes = [_i]
+_lib.mla_abi_version.restype = _i
+_lib.mla_absorb_q.restype = _i
+_lib.mla_absorb_q.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]
+_lib.mla_rope.restype = _i
+_lib.mla_rope.argtypes = [_vp, _vp, _i, _vp, _i, _i, _i, _d, _vp]
+_lib.mla_decode_plan.restype = _i
+_lib.mla_decode_plan.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.POINTER(_i),
+                                 ctypes.POINTER(_i), ctypes.POINTER(ctypes.c_size_t)]
+_lib.mla_decode_paged.restype = _i
+_lib.mla_decode_paged.argtypes = [ctypes.POINTER(DecodeArgs), _vp]
+_lib.mla_out_proj.restype = _i
+_lib.mla_out_proj.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]
+
+EXPORTED = ["mla_status_str", "mla_abi_version", "mla_absorb_q", "mla_rope",
+            "mla_decode_plan", "mla_decode_paged", "mla_out_proj"]
+
+
+def lib():
+    return _lib
+
+
+def abi_version() -> int:
+    return _lib.mla_abi_version()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise MlaError(fn, status)
+
+
+def _stream(stream=None) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MLA_F32
+    if t.dtype == torch.bfloat16:
+        return MLA_BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return MLA_FP8_E4M3
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError("tensors must be contiguous device tensors")
+    return t.data_ptr()
+
+
+# ---------------------------------------------------------------------------
+# the four entry points
+# ---------------------------------------------------------------------------
+
+def absorb_q(q_nope: torch.Tensor, w_uk: torch.Tensor, out_dtype=None,
+             out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """q_lat[n,h,:] = W_UK[h]^T q_nope[n,h,:]; q_nope [n,H,128], w_uk [H,128,512]."""
+    n, H, dh = q_nope.shape
+    dc = w_uk.shape[2]
+    if out is None:
+        out = torch.empty((n, H, dc), dtype=out_dtype or q_nope.dtype, device=q_nope.device)
+    _check("mla_absorb_q", _lib.mla_absorb_q(_ptr(q_nope), _ptr(w_uk), _ptr(out),
+                                             dtype_code(q_nope), dtype_code(out), n, H, dh, dc,
+                                             _stream(stream)))
+    return out
+
+
+def rope(x: torch.Tensor, pos: torch.Tensor, base: float = 10000.0,
+         out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Rotate pairs (2i, 2i+1) of x [n, heads, d_r] at positions pos [n] (int32)."""
+    n, heads, dr = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    _check("mla_rope", _lib.mla_rope(_ptr(x), _ptr(out), dtype_code(x), _ptr(pos), n, heads, dr,
+                                     float(base), _stream(stream)))
+    return out
+
+
+def out_proj(u: torch.Tensor, w_uv: torch.Tensor, out_dtype=None,
+             out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """o[n,h,:] = W_UV[h] u[n,h,:]; u [n,H,512], w_uv [H,128,512]."""
+    n, H, dc = u.shape
+    dh = w_uv.shape[1]
+    if out is None:
+        out = torch.empty((n, H, dh), dtype=out_dtype or w_uv.dtype, device=u.device)
+    _check("mla_out_proj", _lib.mla_out_proj(_ptr(u), _ptr(w_uv), _ptr(out), dtype_code(u),
+                                             dtype_code(w_uv), dtype_code(out), n, H, dh, dc,
+                                             _stream(stream)))
+    return out
+
+
+@dataclass
+class PagedCache:
+    """Device-resident paged latent cache plus its block table."""
+    ckv: torch.Tensor            # [n_pages, 64, 512]  f32 / bf16 / uint8 (E4M3FN codes)
+    kr: torch.Tensor             # [n_pages, 64, 64]   f32 / bf16, already rotated
+    ckv_scale: Optional[torch.Tensor]  # [n_pages, 64] f32 (fp8 only)
+    block_table: torch.Tensor    # [B, max_pages] int32
+    seq_lens: torch.Tensor       # [B] int32
+    max_seq_len: int             # host copy of max(seq_lens)
+    total_tokens: int = 0        # host copy of sum(seq_lens) (planning hint; 0 = unknown)
+
+    @property
+    def n_pages(self) -> int:
+        return self.ckv.shape[0]
+
+
+def make_decode_args(q_lat, q_rope, cache: PagedCache, T: int, softmax_scale: float,
+                     out=None, lse=None, out_dtype=None, split_tokens: int = 0):
+    BT, H, dc = q_lat.shape
+    B = cache.block_table.shape[0]
+    assert BT == B * T, "q_lat must be [B*T, H, d_c]"
+    a = DecodeArgs()
+    a.B, a.T, a.H, a.d_c, a.d_r = B, T, H, dc, q_rope.shape[2]
+    a.page_size = PAGE_SIZE
+    a.n_pages = cache.n_pages
+    a.max_pages_per_seq = cache.block_table.shape[1]
+    a.max_seq_len = int(cache.max_seq_len)
+    a.q_dt = dtype_code(q_lat)
+    a.ckv_dt = dtype_code(cache.ckv)
+    a.kr_dt = dtype_code(cache.kr)
+    if out is not None:
+        a.out_dt = dtype_code(out)
+    elif out_dtype is not None:
+        a.out_dt = MLA_F32 if out_dtype == torch.float32 else MLA_BF16
+    else:
+        a.out_dt = MLA_F32 if a.q_dt == MLA_F32 else MLA_BF16
+    a.split_tokens = split_tokens
+    a.total_tokens = int(cache.total_tokens)
+    a.softmax_scale = softmax_scale
+    a.reserved0 = 0
+    return a
+
+
+def decode_plan(args: DecodeArgs):
+    st, ns, ws = ctypes.c_int(), ctypes.c_int(), ctypes.c_size_t()
+    _check("mla_decode_plan", _lib.mla_decode_plan(ctypes.byref(args), ctypes.byref(st),
+                                                   ctypes.byref(ns), ctypes.byref(ws)))
+    return st.value, ns.value, ws.value
+
+
+def decode_paged(q_lat: torch.Tensor, q_rope: torch.Tensor, cache: PagedCache, T: int,
+                 softmax_scale: float, out: Optional[torch.Tensor] = None,
+                 lse: Optional[torch.Tensor] = None, want_lse: bool = True, out_dtype=None,
+                 split_tokens: int = 0, workspace: Optional[torch.Tensor] = None, stream=None):
+    """u [B*T, H, 512] and lse [B*T, H] of absorbed MLA decode over the paged cache."""
+    a = make_decode_args(q_lat, q_rope, cache, T, softmax_scale, out, lse, out_dtype, split_tokens)
+    BT, H, dc = q_lat.shape
+    if out is None:
+        out = torch.empty((BT, H, dc), dtype=_TORCH_DT[a.out_dt], device=q_lat.device)
+    if lse is None and want_lse:
+        lse = torch.empty((BT, H), dtype=torch.float32, device=q_lat.device)
+    _, _, ws = decode_plan(a)
+    if ws and (workspace is None or workspace.numel() < ws):
+        workspace = torch.empty(ws, dtype=torch.uint8, device=q_lat.device)
+    a.q_lat, a.q_rope = _ptr(q_lat), _ptr(q_rope)
+    a.ckv, a.kr, a.ckv_scale = _ptr(cache.ckv), _ptr(cache.kr), _ptr(cache.ckv_scale)
+    a.block_table, a.seq_lens = _ptr(cache.block_table), _ptr(cache.seq_lens)
+    a.out, a.lse = _ptr(out), _ptr(lse)
+    a.workspace = _ptr(workspace) if ws else None
+    a.workspace_bytes = workspace.numel() if ws else 0
+    _check("mla_decode_paged", _lib.mla_decode_paged(ctypes.byref(a), _stream(stream)))
+    return out, lse
+
+
+# ---------------------------------------------------------------------------
+# upload of stored host arrays (bit patterns) to device tensors
+# ---------------------------------------------------------------------------
+
+def to_device(arr: np.ndarray, dt: str, device="cuda") -> torch.Tensor:
+    """Stored bits -> device tensor of the matching torch dtype (no conversion)."""
+    arr = np.ascontiguousarray(arr)
+    if dt == "f32":
+        return torch.from_numpy(arr.astype(np.float32, copy=False)).to(device)
+    if dt == "bf16":
+        return torch.from_numpy(arr.view(np.int16)).to(device).view(torch.bfloat16)
+    if dt == "fp8":
+        return torch.from_numpy(arr.view(np.uint8)).to(device)
+    if dt == "i32":
+        return torch.from_numpy(arr.astype(np.int32, copy=False)).to(device)
+    raise ValueError(dt)
+
+
+@dataclass
+class DeviceInputs:
+    q_nope: torch.Tensor
+    q_rope: torch.Tensor
+    w_uk: torch.Tensor
+    w_uv: torch.Tensor
+    positions: torch.Tensor
+    cache: PagedCache
+    T: int
+    H: int
+    softmax_scale: float
+
+
+def upload(inp, device="cuda") -> DeviceInputs:
+    """Copy a synthetic workload (mla_latent_kv_35_amd.synth.MlaInputs) to the device."""
+    cfg = inp.cfg
+    cache = PagedCache(
+        ckv=to_device(inp.ckv, cfg.ckv_dt, device),
+        kr=to_device(inp.kr, cfg.kr_dt, device),
+        ckv_scale=None if inp.ckv_scale is None else to_device(inp.ckv_scale, "f32", device),
+        block_table=to_device(inp.block_table, "i32", device),
+        seq_lens=to_device(inp.seq_lens, "i32", device),
+        max_seq_len=int(inp.seq_lens.max()),
+        total_tokens=int(inp.seq_lens.astype(np.int64).sum()),
+    )
+    return DeviceInputs(
+        q_nope=to_device(inp.q_nope, cfg.q_dt, device),
+        q_rope=to_device(inp.q_rope, cfg.q_dt, device),
+        w_uk=to_device(inp.w_uk, cfg.q_dt, device),
+        w_uv=to_device(inp.w_uv, cfg.q_dt, device),
+        positions=to_device(inp.positions, "i32", device),
+        cache=cache, T=cfg.T, H=cfg.H, softmax_scale=cfg.softmax_scale)
+
+
+def decode_step(d: DeviceInputs, split_tokens: int = 0, stream=None, rope_base: float = 10000.0):
+    """One pass of the whole hot path: absorb -> rope -> paged decode (+combine) -> out-proj."""
+    q_lat = absorb_q(d.q_nope, d.w_uk, stream=stream)
+    q_rot = rope(d.q_rope, d.positions, rope_base, stream=stream)
+    u_dtype = torch.float32 if q_lat.dtype == torch.float32 else torch.bfloat16
+    u, lse = decode_paged(q_lat, q_rot, d.cache, d.T, d.softmax_scale, out_dtype=u_dtype,
+                          split_tokens=split_tokens, stream=stream)
+    o = out_proj(u, d.w_uv, out_dtype=torch.float32 if u_dtype == torch.float32 else torch.bfloat16,
+                 stream=stream)
+    return dict(q_lat=q_lat, q_rot=q_rot, u=u, lse=lse, o=o)

@@ -1,0 +1,229 @@
+// C ABI of libmla.so: host-side argument checks, the split planner and the
+// kernel launches. Declarations and semantics: include/mla.h.
+#include <math.h>
+
+#include <algorithm>
+
+#include "mla_internal.h"
+
+namespace mla {
+namespace {
+
+constexpr int kNumCu = 256;           // MI355X compute units
+constexpr size_t kWsAlign = 256;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool is_float_dt(int dt) { return dt == MLA_F32 || dt == MLA_BF16; }
+
+struct Plan {
+  int split_tokens = 0;
+  int n_split = 1;
+  int G = 1;              // 64-row groups (MFMA kernels)
+  size_t part_u_bytes = 0;
+  size_t ws_bytes = 0;
+};
+
+// Checks everything that does not need a device pointer.
+int check_shape(const mla_decode_args* a) {
+  if (!a) return MLA_ERR_NULL;
+  if (a->reserved0 != 0) return MLA_ERR_SHAPE;
+  if (a->B < 1 || a->H < 1 || a->T < 1) return MLA_ERR_SHAPE;
+  if (a->T > 2) return MLA_ERR_UNSUPPORTED;
+  if (a->d_c != kDc || a->d_r != kDr) return MLA_ERR_UNSUPPORTED;
+  if (a->page_size != kPage) return MLA_ERR_UNSUPPORTED;
+  if (a->n_pages < 1 || a->max_pages_per_seq < 1) return MLA_ERR_SHAPE;
+  if (a->max_seq_len < a->T || (int64_t)a->max_seq_len > (int64_t)a->max_pages_per_seq * kPage)
+    return MLA_ERR_SHAPE;
+  if (a->split_tokens < 0 || a->split_tokens % kPage != 0) return MLA_ERR_SHAPE;
+  if (a->total_tokens < 0) return MLA_ERR_SHAPE;
+  if (!(a->softmax_scale > 0.f) || !isfinite(a->softmax_scale)) return MLA_ERR_SHAPE;
+  if ((int64_t)a->T * a->H > (1 << 20)) return MLA_ERR_UNSUPPORTED;
+  // dtype combinations
+  if (a->ckv_dt == MLA_F32) {
+    if (a->kr_dt != MLA_F32 || a->q_dt != MLA_F32 || a->out_dt != MLA_F32) return MLA_ERR_DTYPE;
+  } else if (a->ckv_dt == MLA_BF16) {
+    if (a->kr_dt != MLA_BF16 || a->q_dt != MLA_BF16 || !is_float_dt(a->out_dt)) return MLA_ERR_DTYPE;
+  } else if (a->ckv_dt == MLA_FP8_E4M3) {
+    if (a->kr_dt != MLA_BF16 || a->q_dt != MLA_BF16 || !is_float_dt(a->out_dt)) return MLA_ERR_DTYPE;
+  } else {
+    return MLA_ERR_DTYPE;
+  }
+  return MLA_OK;
+}
+
+Plan make_plan(const mla_decode_args* a) {
+  Plan pl;
+  const int64_t R = (int64_t)a->T * a->H;
+  const int64_t Lmax = a->max_seq_len;
+  const int64_t total = a->total_tokens > 0 ? a->total_tokens : (int64_t)a->B * Lmax;
+  const int64_t pages_total = (total + kPage - 1) / kPage;
+  const int64_t max_pages = (Lmax + kPage - 1) / kPage;
+  pl.G = (int)((R + kRowsPerGroup - 1) / kRowsPerGroup);
+  if (a->split_tokens > 0) {
+    pl.split_tokens = a->split_tokens;
+  } else if (a->ckv_dt == MLA_F32) {
+    // fp32 kernel: one workgroup per (sequence, split, row); aim for ~4 per CU
+    const int64_t want = (4 * kNumCu + a->B * R - 1) / (a->B * R);
+    int64_t sp = (max_pages + want - 1) / want;
+    pl.split_tokens = (int)(std::max<int64_t>(sp, 1) * kPage);
+  } else {
+    // MFMA kernel: units of (sequence, split, 64-row group). Uniform batches
+    // get one unit per CU; ragged ones four per CU so the uneven tails balance.
+    const bool ragged = total * 10 < (int64_t)a->B * Lmax * 9;
+    const int64_t target = ragged ? 4 * kNumCu : kNumCu;
+    int64_t unit_pages = (pl.G * pages_total + target - 1) / target;
+    unit_pages = std::max<int64_t>(unit_pages, 4);
+    unit_pages = std::min<int64_t>(unit_pages, max_pages);
+    pl.split_tokens = (int)(unit_pages * kPage);
+  }
+  pl.n_split = (int)((Lmax + pl.split_tokens - 1) / pl.split_tokens);
+  if (pl.n_split > 1) {
+    const size_t parts = (size_t)a->B * pl.n_split * R;
+    pl.part_u_bytes = align_up(parts * kDc * sizeof(float), kWsAlign);
+    pl.ws_bytes = pl.part_u_bytes + align_up(parts * 2 * sizeof(float), kWsAlign);
+  }
+  return pl;
+}
+
+}  // namespace
+}  // namespace mla
+
+using namespace mla;
+
+extern "C" {
+
+const char* mla_status_str(int status) {
+  switch (status) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_NULL: return "MLA_ERR_NULL: a required pointer is NULL";
+    case MLA_ERR_SHAPE: return "MLA_ERR_SHAPE: a size is out of range or inconsistent";
+    case MLA_ERR_DTYPE: return "MLA_ERR_DTYPE: unsupported dtype combination";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: shape outside what the kernels implement";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE: workspace missing or too small";
+    case MLA_ERR_LAUNCH: return "MLA_ERR_LAUNCH: kernel launch failed";
+    default: return "unknown mla_status";
+  }
+}
+
+int mla_abi_version(void) { return MLA_ABI_VERSION; }
+
+int mla_absorb_q(const void* q_nope, const void* w_uk, void* q_lat, int q_dt, int out_dt,
+                 int n_tok, int H, int d_h, int d_c, void* stream) {
+  if (n_tok < 0 || H < 1) return MLA_ERR_SHAPE;
+  if (d_h != kDh || d_c != kDc) return MLA_ERR_UNSUPPORTED;
+  if (!is_float_dt(q_dt) || !is_float_dt(out_dt)) return MLA_ERR_DTYPE;
+  if (q_dt == MLA_F32 && out_dt != MLA_F32) return MLA_ERR_DTYPE;
+  if (n_tok == 0) return MLA_OK;
+  if (!q_nope || !w_uk || !q_lat) return MLA_ERR_NULL;
+  const hipError_t e = launch_absorb(q_nope, w_uk, q_lat, q_dt == MLA_BF16, out_dt == MLA_BF16,
+                                     n_tok, H, (hipStream_t)stream);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
+}
+
+int mla_rope(const void* x_in, void* x_out, int dt, const int32_t* pos, int n_tok, int n_heads,
+             int d_r, double base, void* stream) {
+  if (n_tok < 0 || n_heads < 1) return MLA_ERR_SHAPE;
+  if (d_r < 2 || d_r > 256 || d_r % 2 != 0) return MLA_ERR_UNSUPPORTED;
+  if (!is_float_dt(dt)) return MLA_ERR_DTYPE;
+  if (!(base > 0.0) || !isfinite(base)) return MLA_ERR_SHAPE;
+  if (n_tok == 0) return MLA_OK;
+  if (!x_in || !x_out || !pos) return MLA_ERR_NULL;
+  const hipError_t e = launch_rope(x_in, x_out, dt == MLA_BF16, pos, n_tok, n_heads, d_r, base,
+                                   (hipStream_t)stream);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
+}
+
+int mla_decode_plan(const mla_decode_args* args, int* split_tokens, int* n_split,
+                    size_t* workspace_bytes) {
+  const int st = check_shape(args);
+  if (st != MLA_OK) return st;
+  const Plan pl = make_plan(args);
+  if (split_tokens) *split_tokens = pl.split_tokens;
+  if (n_split) *n_split = pl.n_split;
+  if (workspace_bytes) *workspace_bytes = pl.ws_bytes;
+  return MLA_OK;
+}
+
+int mla_decode_paged(const mla_decode_args* a, void* stream) {
+  const int st = check_shape(a);
+  if (st != MLA_OK) return st;
+  if (!a->q_lat || !a->q_rope || !a->ckv || !a->kr || !a->block_table || !a->seq_lens || !a->out)
+    return MLA_ERR_NULL;
+  if (a->ckv_dt == MLA_FP8_E4M3 && !a->ckv_scale) return MLA_ERR_NULL;
+  const Plan pl = make_plan(a);
+  if (pl.n_split > 1) {
+    if (!a->workspace || a->workspace_bytes < pl.ws_bytes) return MLA_ERR_WORKSPACE;
+    if (((uintptr_t)a->workspace) % kWsAlign != 0) return MLA_ERR_WORKSPACE;
+  }
+
+  DecodeParams p{};
+  p.q_lat = a->q_lat;
+  p.q_rope = a->q_rope;
+  p.ckv = a->ckv;
+  p.kr = a->kr;
+  p.ckv_scale = a->ckv_scale;
+  p.block_table = a->block_table;
+  p.seq_lens = a->seq_lens;
+  p.out = a->out;
+  p.lse = a->lse;
+  p.part_u = pl.n_split > 1 ? (float*)a->workspace : nullptr;
+  p.part_ml = pl.n_split > 1 ? (float*)((char*)a->workspace + pl.part_u_bytes) : nullptr;
+  p.B = a->B;
+  p.T = a->T;
+  p.H = a->H;
+  p.R = a->T * a->H;
+  p.G = pl.G;
+  p.n_split = pl.n_split;
+  p.split_tokens = pl.split_tokens;
+  p.n_pages = a->n_pages;
+  p.max_pages = a->max_pages_per_seq;
+  p.max_seq_len = a->max_seq_len;
+  p.out_bf16 = a->out_dt == MLA_BF16;
+  p.scale_log2 = a->softmax_scale * kLog2e;
+  const int64_t units = (int64_t)a->B * pl.n_split * pl.G;
+  if (units > (int64_t)1 << 30) return MLA_ERR_UNSUPPORTED;
+  p.n_units = (int)units;
+  p.per_xcd = (int)((units + kNumXcd - 1) / kNumXcd);
+
+  const hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (a->ckv_dt == MLA_F32) e = launch_decode_simple_f32(p, s);
+  else if (a->ckv_dt == MLA_BF16) e = launch_decode_mfma_bf16(p, s);
+  else return MLA_ERR_UNSUPPORTED;
+  if (e != hipSuccess) return MLA_ERR_LAUNCH;
+  if (pl.n_split > 1) {
+    CombineParams c{};
+    c.part_u = p.part_u;
+    c.part_ml = p.part_ml;
+    c.out = a->out;
+    c.lse = a->lse;
+    c.seq_lens = a->seq_lens;
+    c.rows = a->B * p.R;
+    c.R = p.R;
+    c.T = a->T;
+    c.n_split = pl.n_split;
+    c.split_tokens = pl.split_tokens;
+    c.max_seq_len = a->max_seq_len;
+    c.max_pages = a->max_pages_per_seq;
+    c.out_bf16 = p.out_bf16;
+    e = launch_combine(c, s);
+    if (e != hipSuccess) return MLA_ERR_LAUNCH;
+  }
+  return MLA_OK;
+}
+
+int mla_out_proj(const void* u, const void* w_uv, void* o, int u_dt, int w_dt, int o_dt, int n_tok,
+                 int H, int d_h, int d_c, void* stream) {
+  if (n_tok < 0 || H < 1) return MLA_ERR_SHAPE;
+  if (d_h != kDh || d_c != kDc) return MLA_ERR_UNSUPPORTED;
+  if (!is_float_dt(u_dt) || !is_float_dt(w_dt) || !is_float_dt(o_dt)) return MLA_ERR_DTYPE;
+  if (w_dt == MLA_F32 && (u_dt != MLA_F32 || o_dt != MLA_F32)) return MLA_ERR_DTYPE;
+  if (n_tok == 0) return MLA_OK;
+  if (!u || !w_uv || !o) return MLA_ERR_NULL;
+  const hipError_t e = launch_out_proj(u, w_uv, o, u_dt == MLA_BF16, w_dt == MLA_BF16,
+                                       o_dt == MLA_BF16, n_tok, H, (hipStream_t)stream);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
+}
+
+}  // extern "C"

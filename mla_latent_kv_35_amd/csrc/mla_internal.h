@@ -1,0 +1,69 @@
+// Internal host-side interfaces between the C ABI (mla_api.hip) and the
+// kernel translation units. Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/mla.h"
+
+namespace mla {
+
+constexpr int kPage = 64;
+constexpr int kDc = 512;
+constexpr int kDr = 64;
+constexpr int kDh = 128;
+constexpr int kRowsPerGroup = 64;   // query rows per decode workgroup (MFMA kernel)
+constexpr int kNumXcd = 8;          // MI355X: 8 XCDs, workgroups dispatched round-robin
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Everything a decode kernel needs; filled by the host planner.
+struct DecodeParams {
+  const void* q_lat;        // [B][R][512]
+  const void* q_rope;       // [B][R][64]
+  const void* ckv;          // [n_pages][64][512]
+  const void* kr;           // [n_pages][64][64]
+  const float* ckv_scale;   // [n_pages][64] (fp8 only)
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  void* out;                // [B][R][512]
+  float* lse;               // [B][R] or null
+  float* part_u;            // [B][n_split][R][512] fp32 (n_split > 1)
+  float* part_ml;           // [B][n_split][R][2]   fp32 (m in log2 units, l)
+  int B, T, H, R;           // R = T*H query rows per sequence
+  int G;                    // row groups per sequence (MFMA kernel)
+  int n_split, split_tokens;
+  int n_pages, max_pages, max_seq_len;
+  int out_bf16;
+  int n_units;              // work units actually present
+  int per_xcd;              // grid = per_xcd * 8 (XCD-major unit numbering)
+  float scale_log2;         // softmax_scale * log2(e)
+};
+
+struct CombineParams {
+  const float* part_u;
+  const float* part_ml;
+  void* out;
+  float* lse;
+  const int32_t* seq_lens;  // splits at or past L_b hold no partials
+  int rows;                 // B*R
+  int R, T, n_split, split_tokens;
+  int max_seq_len, max_pages;
+  int out_bf16;
+};
+
+hipError_t launch_decode_mfma_bf16(const DecodeParams& p, hipStream_t s);
+hipError_t launch_decode_mfma_fp8(const DecodeParams& p, hipStream_t s);
+hipError_t launch_decode_simple_f32(const DecodeParams& p, hipStream_t s);
+hipError_t launch_combine(const CombineParams& p, hipStream_t s);
+
+hipError_t launch_rope(const void* x_in, void* x_out, int bf16, const int32_t* pos, int n_tok,
+                       int n_heads, int d_r, double base, hipStream_t s);
+hipError_t launch_absorb(const void* q_nope, const void* w_uk, void* q_lat, int in_bf16,
+                         int out_bf16, int n_tok, int H, hipStream_t s);
+hipError_t launch_out_proj(const void* u, const void* w_uv, void* o, int u_bf16, int w_bf16,
+                           int o_bf16, int n_tok, int H, hipStream_t s);
+
+}  // namespace mla

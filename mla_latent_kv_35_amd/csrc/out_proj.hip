@@ -1,0 +1,107 @@
+// Per-head value up-projection after latent aggregation (PaperTrace "02 ·
+// DeepSeek-V2 analysis", section 6.1: each head aggregates latents with its
+// own weights first, then applies its own matrix): o[n][h][:] = W_UV[h] u[n][h][:].
+//
+// bf16: one workgroup per (head h, 64 output dims, 256-token block); each wave
+// owns 16 output dims. Both MFMA operands are contiguous along the reduced
+// latent axis in memory (u rows and W_UV rows), so they load straight from
+// global memory. fp32: plain fp32 FMA.
+#include "mla_device.h"
+#include "mla_internal.h"
+
+namespace mla {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kTokBlock = 256;
+
+__device__ __forceinline__ bf16x8_t load_row8(const void* base, size_t off, bool bf16) {
+  if (bf16) return load_bf16x8((const uint16_t*)base + off);
+  const f32x4_t lo = *(const f32x4_t*)((const float*)base + off);
+  const f32x4_t hi = *(const f32x4_t*)((const float*)base + off + 4);
+  bf16x8_t r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r[i] = (__bf16)lo[i];
+    r[i + 4] = (__bf16)hi[i];
+  }
+  return r;
+}
+
+template <bool U_BF16, bool O_BF16>
+__global__ __launch_bounds__(kThreads) void out_proj_bf16_kernel(const void* __restrict__ u,
+                                                                 const uint16_t* __restrict__ wuv,
+                                                                 void* __restrict__ o, int n_tok,
+                                                                 int H) {
+  const int h = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int i16 = lane & 15, G4 = lane >> 4;
+  const int j = 64 * blockIdx.y + 16 * w + i16;       // this lane's output dim (B column)
+  const int n_base = blockIdx.z * kTokBlock;
+
+  bf16x8_t bw[16];
+  const uint16_t* wrow = wuv + ((size_t)h * kDh + j) * kDc + 8 * G4;
+#pragma unroll
+  for (int ks = 0; ks < 16; ++ks) bw[ks] = load_bf16x8(wrow + 32 * ks);
+
+  const int n_end = min(n_tok, n_base + kTokBlock);
+  for (int n0 = n_base; n0 < n_end; n0 += 16) {
+    const int na = n0 + i16;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) {
+      bf16x8_t a = (bf16x8_t){0, 0, 0, 0, 0, 0, 0, 0};
+      if (na < n_tok) a = load_row8(u, ((size_t)na * H + h) * kDc + 32 * ks + 8 * G4, U_BF16);
+      acc = mfma16x16x32(a, bw[ks], acc);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int n = n0 + 4 * G4 + i;
+      if (n < n_tok) {
+        const size_t off = ((size_t)n * H + h) * kDh + j;
+        if (O_BF16) ((uint16_t*)o)[off] = f2bf(acc[i]);
+        else ((float*)o)[off] = acc[i];
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(kDh) void out_proj_f32_kernel(const float* __restrict__ u,
+                                                          const float* __restrict__ wuv,
+                                                          float* __restrict__ o, int H) {
+  __shared__ float us[kDc];
+  const int nh = blockIdx.x;
+  const int h = nh % H;
+  for (int d = threadIdx.x; d < kDc; d += kDh) us[d] = u[(size_t)nh * kDc + d];
+  __syncthreads();
+  const int j = threadIdx.x;
+  const float* wr = wuv + ((size_t)h * kDh + j) * kDc;
+  float acc = 0.f;
+  for (int d = 0; d < kDc; ++d) acc = fmaf(wr[d], us[d], acc);
+  o[(size_t)nh * kDh + j] = acc;
+}
+
+}  // namespace
+
+hipError_t launch_out_proj(const void* u, const void* w_uv, void* o, int u_bf16, int w_bf16,
+                           int o_bf16, int n_tok, int H, hipStream_t s) {
+  if (n_tok == 0) return hipSuccess;
+  if (w_bf16) {
+    dim3 grid(H, kDh / 64, (n_tok + kTokBlock - 1) / kTokBlock);
+    const uint16_t* w = (const uint16_t*)w_uv;
+    if (u_bf16 && o_bf16)
+      hipLaunchKernelGGL((out_proj_bf16_kernel<true, true>), grid, dim3(kThreads), 0, s, u, w, o, n_tok, H);
+    else if (u_bf16)
+      hipLaunchKernelGGL((out_proj_bf16_kernel<true, false>), grid, dim3(kThreads), 0, s, u, w, o, n_tok, H);
+    else if (o_bf16)
+      hipLaunchKernelGGL((out_proj_bf16_kernel<false, true>), grid, dim3(kThreads), 0, s, u, w, o, n_tok, H);
+    else
+      hipLaunchKernelGGL((out_proj_bf16_kernel<false, false>), grid, dim3(kThreads), 0, s, u, w, o, n_tok, H);
+  } else {
+    hipLaunchKernelGGL(out_proj_f32_kernel, dim3(n_tok * H), dim3(kDh), 0, s, (const float*)u,
+                       (const float*)w_uv, (float*)o, H);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,70 @@
+// Rotary embedding of the decoupled rope part (PaperTrace "02 · DeepSeek-V2
+// analysis", section 1.3, eq. 14-15): coordinate pairs (2i, 2i+1) are rotated
+// by pos * base^(-2i/d_r) (CSDN "DeepSeek-V3 structure and engineering",
+// section 2(3)). Angles, cos and sin are fp64 (at position 131071 an fp32
+// angle is off by up to 0.008 rad); the rotation is fp64, rounded to fp32 and
+// then (for bf16 storage) to bf16.
+#include "mla_device.h"
+#include "mla_internal.h"
+
+namespace mla {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxHalf = 128;
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void rope_kernel(const void* x_in, void* x_out,
+                                                        const int32_t* pos, int n_heads, int d_r,
+                                                        double base) {
+  __shared__ double cs[kMaxHalf][2];
+  const int n = blockIdx.x;
+  const int half = d_r / 2;
+  const double pn = (double)pos[n];
+  for (int i = threadIdx.x; i < half; i += kThreads) {
+    const double theta = pow(base, -2.0 * (double)i / (double)d_r);
+    double s, c;
+    sincos(pn * theta, &s, &c);
+    cs[i][0] = c;
+    cs[i][1] = s;
+  }
+  __syncthreads();
+  const size_t row0 = (size_t)n * n_heads * d_r;
+  for (int e = threadIdx.x; e < n_heads * half; e += kThreads) {
+    const int h = e / half, i = e % half;
+    const size_t o = row0 + (size_t)h * d_r + 2 * i;
+    double x0, x1;
+    if (BF16) {
+      x0 = bf2f(((const uint16_t*)x_in)[o]);
+      x1 = bf2f(((const uint16_t*)x_in)[o + 1]);
+    } else {
+      x0 = ((const float*)x_in)[o];
+      x1 = ((const float*)x_in)[o + 1];
+    }
+    const double c = cs[i][0], s = cs[i][1];
+    const float y0 = (float)(x0 * c - x1 * s);
+    const float y1 = (float)(x0 * s + x1 * c);
+    if (BF16) {
+      ((uint16_t*)x_out)[o] = f2bf(y0);
+      ((uint16_t*)x_out)[o + 1] = f2bf(y1);
+    } else {
+      ((float*)x_out)[o] = y0;
+      ((float*)x_out)[o + 1] = y1;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_rope(const void* x_in, void* x_out, int bf16, const int32_t* pos, int n_tok,
+                       int n_heads, int d_r, double base, hipStream_t s) {
+  if (bf16)
+    hipLaunchKernelGGL(rope_kernel<true>, dim3(n_tok), dim3(kThreads), 0, s, x_in, x_out, pos,
+                       n_heads, d_r, base);
+  else
+    hipLaunchKernelGGL(rope_kernel<false>, dim3(n_tok), dim3(kThreads), 0, s, x_in, x_out, pos,
+                       n_heads, d_r, base);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,114 @@
+"""The C-ABI library on the host (no GPU needed): it loads, exports every symbol
+include/mla.h declares, and its host-side planner and argument checks behave.
+Nothing here launches a kernel: every decode call below is rejected by the
+host checks before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "mla_latent_kv_35_amd", "libmla.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libmla.so not built")
+
+
+def header_functions():
+    txt = open(os.path.join(ROOT, "include", "mla.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_\w+)\s*\(", txt)))
+
+
+@pytest.fixture(scope="module")
+def B():
+    from mla_latent_kv_35_amd import binding
+    return binding
+
+
+def test_exports_every_declared_symbol(B):
+    declared = header_functions()
+    assert declared == sorted(B.EXPORTED)
+    lib = ctypes.CDLL(LIB)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(B):
+    assert B.abi_version() == 1
+    for code in range(7):
+        assert B.lib().mla_status_str(code).decode().startswith("MLA_")
+    assert b"unknown" in B.lib().mla_status_str(99)
+
+
+def _args(mod, **kw):
+    a = mod.DecodeArgs()
+    a.B, a.T, a.H, a.d_c, a.d_r = 32, 1, 128, 512, 64
+    a.page_size, a.n_pages, a.max_pages_per_seq, a.max_seq_len = 64, 2048, 64, 4096
+    a.q_dt = a.ckv_dt = a.kr_dt = a.out_dt = mod.MLA_BF16
+    a.split_tokens, a.total_tokens, a.softmax_scale, a.reserved0 = 0, 0, 192 ** -0.5, 0
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_plan_for_the_five_workloads(B):
+    # DeepSeek-V2 layer: 64 (sequence, 64-row group) pairs x 4 splits = 256 units
+    assert B.decode_plan(_args(B))[:2] == (1024, 4)
+    # 128K: 8 pairs x 32 splits
+    assert B.decode_plan(_args(B, B=4, n_pages=8192, max_pages_per_seq=2048,
+                                   max_seq_len=131072))[:2] == (4096, 32)
+    # two-token fp8: 4 row groups x 128 sequences, no split
+    st, ns, ws = B.decode_plan(_args(B, B=128, T=2, ckv_dt=B.MLA_FP8_E4M3, n_pages=16384,
+                                     max_pages_per_seq=128, max_seq_len=8192))
+    assert ns == 1 and ws == 0
+    # ragged: planned from the token total, about four units per CU
+    st, ns, ws = B.decode_plan(_args(B, B=64, n_pages=16522, max_pages_per_seq=497,
+                                     max_seq_len=31804, total_tokens=1055283))
+    assert st % 64 == 0 and ns == -(-31804 // st)
+    parts = 64 * ns * 128
+    assert ws == ((parts * 512 * 4 + 255) // 256) * 256 + ((parts * 8 + 255) // 256) * 256
+    # fp32 tiny
+    st, ns, _ = B.decode_plan(_args(B, B=1, H=16, q_dt=0, ckv_dt=0, kr_dt=0, out_dt=0,
+                                    n_pages=4, max_pages_per_seq=4, max_seq_len=256))
+    assert st % 64 == 0 and ns == -(-256 // st)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("T", 3, 4), ("d_c", 256, 4), ("page_size", 32, 4), ("max_seq_len", 0, 2),
+    ("max_seq_len", 64 * 64 + 1, 2), ("split_tokens", 100, 2), ("reserved0", 1, 2),
+    ("softmax_scale", 0.0, 2), ("kr_dt", 0, 3), ("ckv_dt", 7, 3), ("B", 0, 2),
+])
+def test_plan_rejects_bad_shapes(B, field, value, status):
+    st = B.lib().mla_decode_plan(ctypes.byref(_args(B, **{field: value})), None, None, None)
+    assert st == status
+
+
+def test_decode_rejects_before_launch(B):
+    fake = 0x1000
+    a = _args(B)
+    # null pointers
+    assert B.lib().mla_decode_paged(ctypes.byref(a), None) == 1
+    for name in ("q_lat", "q_rope", "ckv", "kr", "block_table", "seq_lens", "out"):
+        setattr(a, name, fake)
+    # the plan needs a workspace (4 splits) and none is given
+    assert B.lib().mla_decode_paged(ctypes.byref(a), None) == 5
+    a.workspace, a.workspace_bytes = fake, 16
+    assert B.lib().mla_decode_paged(ctypes.byref(a), None) == 5
+    # fp8 without scales
+    a.ckv_dt = B.MLA_FP8_E4M3
+    assert B.lib().mla_decode_paged(ctypes.byref(a), None) == 1
+    assert B.lib().mla_decode_paged(None, None) == 1
+
+
+def test_dense_entry_points_reject_before_launch(B):
+    L = B.lib()
+    assert L.mla_absorb_q(None, None, None, 1, 1, 4, 128, 128, 512, None) == 1
+    assert L.mla_absorb_q(None, None, None, 1, 1, 4, 128, 64, 512, None) == 4
+    assert L.mla_absorb_q(None, None, None, 0, 1, 4, 128, 128, 512, None) == 3
+    assert L.mla_absorb_q(None, None, None, 1, 1, 0, 128, 128, 512, None) == 0   # empty: no-op
+    assert L.mla_rope(None, None, 1, None, 4, 128, 63, 10000.0, None) == 4
+    assert L.mla_rope(None, None, 1, None, 4, 128, 64, -1.0, None) == 2
+    assert L.mla_rope(None, None, 1, None, 4, 128, 64, 10000.0, None) == 1
+    assert L.mla_out_proj(None, None, None, 1, 0, 1, 4, 128, 128, 512, None) == 3
+    assert L.mla_out_proj(None, None, None, 1, 1, 1, -1, 128, 128, 512, None) == 2
