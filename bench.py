@@ -1,0 +1,245 @@
+"""Benchmark of the MLA absorbed-decode hot path on one MI355X.
+
+One step = the whole path over one batch: mla_absorb_q -> mla_rope ->
+mla_decode_paged (split kernel + log-sum-exp combine) -> mla_out_proj, on the
+DeepSeek-V2-shaped layer B=32, H=128, S=4096, bf16 (synthetic, seeded; see
+mla_latent_kv_35_amd.synth). Inputs are resident in HBM before timing starts;
+the step cycles through enough replicas of the 151 MB paged cache that the
+256 MB Infinity Cache cannot serve it.
+
+Prints one JSON line: whole-step throughput (tokens/s), the decode's HBM
+bandwidth on latent-cache reads, the roofline of the dominant kernel (timed
+with HIP events on the stream it runs on) and the CPU oracle's throughput on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0       # dense bf16 MFMA
+METRIC = "MLA decode tokens/s + achieved HBM GB/s (% of peak), B=32 H=128 S=4096 bf16"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic_dsv2_layer.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--config", default="dsv2_layer")
+    ap.add_argument("--replicas", type=int, default=0, help="cache copies cycled (0 = auto)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="budget for the CPU-oracle baseline sample (0 = skip)")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB, 5 times "
+                         "(the known-size reference for HBM byte counters)")
+    return ap.parse_args()
+
+
+def copy_probe(mib: int) -> None:
+    import torch
+    n = mib * (1 << 20)
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "launches": 5}))
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for f in ("decode_mfma.hip", "mla_device.h", "mla_internal.h"):
+        with open(os.path.join(ROOT, "mla_latent_kv_35_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(launch_bytes: float):
+    """HBM bytes per decode launch from the committed rocprofv3 counter runs,
+    valid only while the kernel sources are the ones they were taken on."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_digest") != kernel_source_digest():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, budget_s: float):
+    """The oracle as it stands, on whole sequences of the same workload until
+    the time budget is used; tokens/s in the benchmark's unit."""
+    from threadpoolctl import threadpool_info
+    from oracle import mla_oracle as O
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    done, t0 = 0, time.perf_counter()
+    while done < inp.cfg.B and (time.perf_counter() - t0) < budget_s:
+        O.decode_step(inp, batches=[done])
+        done += 1
+    el = time.perf_counter() - t0
+    return {"value": round(done * inp.cfg.T / el, 3), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{done} of {inp.cfg.B} sequences of {inp.cfg.name} "
+                      f"(L={int(inp.seq_lens[0])}, H={inp.cfg.H}), float64 numpy, {el:.1f} s"}
+
+
+def main():
+    a = parse()
+    if a.copy_probe_mb:
+        copy_probe(a.copy_probe_mb)
+        return
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {a.gpus}); the decode path "
+              "is single-GPU by design", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from mla_latent_kv_35_amd import binding as mla, synth
+    from oracle import mla_oracle as O
+
+    torch.cuda.set_device(0)
+    inp = synth.make_inputs(a.config)
+    cfg = inp.cfg
+    d = mla.upload(inp)
+    cache_bytes = inp.total_tokens * O.decode_cache_bytes_per_token(cfg.ckv_dt, cfg.kr_dt)
+    R = a.replicas or max(1, int(np.ceil(640e6 / cache_bytes)))
+    caches = [d.cache]
+    for _ in range(R - 1):
+        c = d.cache
+        caches.append(mla.PagedCache(c.ckv.clone(), c.kr.clone(),
+                                     None if c.ckv_scale is None else c.ckv_scale.clone(),
+                                     c.block_table.clone(), c.seq_lens.clone(), c.max_seq_len,
+                                     c.total_tokens))
+    stream = torch.cuda.current_stream()
+    u_dtype = torch.float32 if cfg.q_dt == "f32" else torch.bfloat16
+    # outputs and workspace allocated once, outside the timed region
+    BT, H = cfg.B * cfg.T, cfg.H
+    q_lat = torch.empty((BT, H, 512), dtype=d.q_nope.dtype, device="cuda")
+    q_rot = torch.empty_like(d.q_rope)
+    u = torch.empty((BT, H, 512), dtype=u_dtype, device="cuda")
+    lse = torch.empty((BT, H), dtype=torch.float32, device="cuda")
+    o = torch.empty((BT, H, 128), dtype=u_dtype, device="cuda")
+    _, n_split, ws = mla.decode_plan(mla.make_decode_args(q_lat, q_rot, d.cache, cfg.T,
+                                                          cfg.softmax_scale, out=u))
+    work = torch.empty(max(ws, 256), dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        c = caches[i % R]
+        mla.absorb_q(d.q_nope, d.w_uk, out=q_lat)
+        mla.rope(d.q_rope, d.positions, out=q_rot)
+        mla.decode_paged(q_lat, q_rot, c, cfg.T, cfg.softmax_scale, out=u, lse=lse,
+                         workspace=work)
+        mla.out_proj(u, d.w_uv, out=o)
+
+    def decode_only(i):
+        mla.decode_paged(q_lat, q_rot, caches[i % R], cfg.T, cfg.softmax_scale, out=u, lse=lse,
+                         workspace=work)
+
+    def capture(fn, n):
+        # HIP graph of n consecutive calls (no allocation or memset inside)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn(0)
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for j in range(n):
+                fn(j)
+        return g
+
+    per_graph = R * max(1, 10 // R)
+    steps = max(1, a.steps)
+    n_rep, rem = divmod(steps, per_graph)
+    g_step = capture(step, per_graph)
+    g_rem = capture(step, rem) if rem else None
+    for _ in range(max(1, -(-a.warmup // per_graph))):
+        g_step.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n_rep):
+        g_step.replay()
+    if g_rem is not None:
+        g_rem.replay()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+
+    # eager launches of the same step, for reference (host launch overhead included)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    el_eager = time.perf_counter() - t1
+
+    # dominant kernel: back-to-back decode launches, timed with events on their stream
+    g_dec = capture(decode_only, per_graph)
+    g_dec.replay()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    n_dec = max(1, n_rep)
+    for _ in range(n_dec):
+        g_dec.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    dur_ms = {"decode": e0.elapsed_time(e1) / (n_dec * per_graph)}
+
+    tokens = cfg.B * cfg.T
+    value = tokens * steps / el
+    dec_s = dur_ms["decode"] * 1e-3
+    achieved = cache_bytes / dec_s / 1e9
+    flops = inp.total_tokens * cfg.H * cfg.T * O.decode_flops_per_row_token()
+    traffic = load_traffic(cache_bytes)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(el / steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8+bf16"}[cfg.ckv_dt],
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "B": cfg.B, "H": cfg.H, "T": cfg.T,
+                   "seq_len": cfg.seq_len, "d_c": 512, "d_r": 64, "page": 64,
+                   "cache_dtype": cfg.ckv_dt, "n_split": n_split, "cache_replicas": R},
+        "hbm_gbps": round(achieved, 1),
+        "hbm_pct_of_peak": round(100 * achieved / PEAK_HBM_GBPS, 2),
+        "decode_ms": round(dur_ms["decode"], 5),
+        "eager_ms_per_step": round(el_eager / steps * 1e3, 5),
+        "launch": "hip graph of %d steps per replay" % per_graph,
+        "roofline": {
+            "kernel": "mla_decode_paged (split-KV kernel + log-sum-exp combine)",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBPS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": cache_bytes,
+            "mfma_tflops": round(flops / dec_s / 1e12, 1),
+            "mfma_frac_bf16": round(flops / dec_s / 1e12 / PEAK_BF16_TFLOPS, 4),
+        },
+    }
+    if a.cpu_seconds > 0:
+        out["cpu_baseline"] = cpu_baseline(inp, a.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -284,3 +284,49 @@ def test_out_of_range_length_and_page_give_nan(mla):
         assert not np.isnan(uh[0]).any() and not np.isnan(lh[0]).any()
         assert np.isnan(uh[1]).all() and np.isnan(lh[1]).all()
         assert np.isnan(uh[2]).all() and np.isnan(lh[2]).all()
+
+
+# --------------------------------------------------------------------------
+# HIP graph capture of the whole step: every replay equals the eager result
+# --------------------------------------------------------------------------
+
+def test_graph_replay_matches_eager(mla):
+    inp = _ragged(seed=61, B=4, seq_len=900)
+    d = mla.upload(inp)
+    eager = mla.decode_step(d, split_tokens=128)
+    torch.cuda.synchronize()
+    ref = {k: v.clone() for k, v in eager.items()}
+    bufs = {}
+
+    def run():
+        q_lat = mla.absorb_q(d.q_nope, d.w_uk, out=bufs["q_lat"])
+        q_rot = mla.rope(d.q_rope, d.positions, out=bufs["q_rot"])
+        mla.decode_paged(q_lat, q_rot, d.cache, d.T, d.softmax_scale, out=bufs["u"],
+                         lse=bufs["lse"], split_tokens=128, workspace=bufs["ws"])
+        mla.out_proj(bufs["u"], d.w_uv, out=bufs["o"])
+
+    for k in ("q_lat", "q_rot", "u", "lse", "o"):
+        bufs[k] = torch.empty_like(ref[k])
+    a = mla.make_decode_args(bufs["q_lat"], bufs["q_rot"], d.cache, d.T, d.softmax_scale,
+                             out=bufs["u"], split_tokens=128)
+    bufs["ws"] = torch.empty(max(mla.decode_plan(a)[2], 256), dtype=torch.uint8, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for rep in range(4):
+        for k in bufs:
+            if k != "ws":
+                bufs[k].fill_(float("nan") if bufs[k].is_floating_point() else 0)
+        junk = mla.decode_step(d, split_tokens=64)       # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in ref:
+            assert torch.equal(bufs[k].view(torch.int16) if bufs[k].dtype == torch.bfloat16 else bufs[k],
+                               ref[k].view(torch.int16) if ref[k].dtype == torch.bfloat16 else ref[k]), (rep, k)
+        del junk
