@@ -1,50 +1,63 @@
 // Paged absorbed-MLA decode on gfx950 bf16 MFMA.
 //
-// One workgroup (4 waves, 256 threads) owns a work unit (sequence b, split k,
-// group g of 64 query rows). It streams the split's 64-token cache pages
-// through LDS (double buffered, asynchronous 16-byte global->LDS copies) and,
-// per page:
-//   1. scores  S^T[token][row] = K[token][576] . Q^T[576][row] on MFMA
-//      16x16x32 (the 512 latent + 64 rope features of the V2 analysis page's
-//      576-element cache, section 1.3); each wave does 32 tokens x 32 rows
-//      with its rows' absorbed queries held in registers;
-//   2. online softmax in fp32 (log2 domain, scale folded in): per-row page
-//      maxima exchanged through LDS, probabilities rounded once to bf16 and
-//      staged in LDS, row sums taken from the rounded values;
-//   3. aggregation U[row][d] += P[row][token] C[token][d] on MFMA with the
-//      latent tile read transposed (ds_read_b64_tr_b16); each wave owns 128
-//      of the 512 latent dimensions for all 64 rows (section 6.1: each head
-//      aggregates latents with its own weights).
+// One workgroup owns a work unit (sequence b, split k, group g of 64 query
+// rows) and streams the split's cache through LDS in tiles of 32 tokens
+// (half a page): 512 latent + 64 rope bf16 per token, the 576-element cache
+// of PaperTrace "02 · DeepSeek-V2 analysis", section 1.3.
+//
+// The workgroup's 8 waves form two teams that work one tile apart, so that on
+// every SIMD one wave's softmax and LDS traffic overlap the other wave's MFMAs:
+//
+//  * score team (waves 0-3): wave (hh, th) holds the absorbed queries of rows
+//    32*hh..+31 in registers and, for tile j, computes the scores of its 16
+//    tokens S^T[token][row] = K[token][576] . Q^T[576][row] on MFMA 16x16x32,
+//    exchanges per-row tile maxima with its partner wave through LDS, and
+//    writes bf16 probabilities p = 2^(z - m) (log2 units, scale folded in,
+//    section 1.3 eq. 18) and the rows' rescale factors to LDS;
+//  * aggregation team (waves 4-7): wave v owns latent dims 128*v..+127 of all
+//    64 rows and, during step j, accumulates U[row][d] += P[row][token]
+//    C[token][d] for tile j-1 on MFMA, reading the latent tile transposed
+//    (ds_read_b64_tr_b16) -- each head aggregates latents with its own weights
+//    (section 6.1). Between its MFMA groups it issues the asynchronous copies
+//    of tile j+2.
+//
+// Per step: barrier X (tile j resident, P(j-1) published), barrier Y (score
+// team's tile maxima published). Four tile buffers keep two tiles in flight
+// while two are in use. All barriers order LDS only; the page copies are
+// waited for explicitly with vmcnt by the waves that issued them.
+//
 // The split ends by writing either u = U / l and lse, or fp32 partials
 // (m, l, U) for the log-sum-exp combine kernel.
-//
-// LDS (157,696 B of gfx950's 160 KiB): two page tiles of 73,728 B (latent rows
-// of 1,024 B and rope rows of 128 B, XOR-swizzled at 16-B granularity so the
-// score reads and the transposed reads are bank-conflict free), the bf16
-// probability tile and two small per-row exchange arrays.
 #include "mla_device.h"
 #include "mla_internal.h"
 
 namespace mla {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kLatBytes = kPage * kDc * 2;          // 65536
-constexpr int kRopeBytes = kPage * kDr * 2;         // 8192
-constexpr int kTileBytes = kLatBytes + kRopeBytes;  // 73728
-constexpr int kPStride = 144;                       // bytes per probability row
-constexpr int kPBytes = kRowsPerGroup * kPStride;   // 9216
-constexpr int kOffP = 2 * kTileBytes;               // 147456
-constexpr int kOffRed = kOffP + kPBytes;            // per-row page maxima [2][64] f32
-constexpr int kOffLsum = kOffRed + 2 * 64 * 4;      // per-row sums [2][64] f32
-constexpr int kOffAlpha = kOffLsum + 2 * 64 * 4;    // per-row rescale factor [64] f32
-constexpr int kOffM = kOffAlpha + 64 * 4;           // per-row final reference max [64] f32
-constexpr int kLdsBytes = kOffM + 64 * 4;           // 158208
+constexpr int kThreads = 512;
+constexpr int kTileTok = 32;
+constexpr int kLatTile = kTileTok * 1024;           // 32768: latent rows of 1 KB
+constexpr int kRopeTile = kTileTok * 128;           // 4096: rope rows of 128 B
+constexpr int kTileBytes = kLatTile + kRopeTile;    // 36864
+constexpr int kNumBuf = 4;
+constexpr int kPStride = 80;                        // bytes per probability row (32 bf16 + pad)
+constexpr int kPBytes = kRowsPerGroup * kPStride;   // 5120
+constexpr int kOffP = kNumBuf * kTileBytes;         // 147456: P[2]
+constexpr int kOffAlpha = kOffP + 2 * kPBytes;      // alpha[2][64] f32
+constexpr int kOffRed = kOffAlpha + 2 * 64 * 4;     // tile maxima [2][64] f32
+constexpr int kOffLsum = kOffRed + 2 * 64 * 4;      // row sums [2][64] f32
+constexpr int kOffM = kOffLsum + 2 * 64 * 4;        // final reference max [64] f32
+constexpr int kOffIds = kOffM + 64 * 4;             // page ids of the split
+constexpr int kLdsBytes = kOffIds + kMaxSplitPages * 4;   // 163584
+static_assert(kLdsBytes <= 163840, "LDS budget");
 
-// The running reference max of a row only moves when a page's max exceeds it
+// DMA copies per tile per aggregation wave: 8 latent rows + 1 rope block.
+constexpr int kDmaPerWave = 9;
+
+// The running reference max of a row only moves when a tile's max exceeds it
 // by more than kLazyMax (log2 units): probabilities are then bounded by
 // 2^kLazyMax, which fp32 sums and bf16 probabilities hold exactly as well,
-// and the accumulator rescale runs on the first page and on rare jumps only.
+// and the accumulator rescale runs on the first tile and on rare jumps only.
 // u, l and lse do not depend on the reference.
 constexpr float kLazyMax = 8.0f;
 
@@ -59,38 +72,46 @@ __device__ __forceinline__ int swz_lat(int s) {
 // Rope rows (128 B): chunk j (0..7) of token t lives at chunk j ^ ((t>>1)&7).
 __device__ __forceinline__ int swz_rope(int t) { return (t >> 1) & 7; }
 
-__device__ __forceinline__ void block_sync() { __syncthreads(); }
-
-// Issue the asynchronous copy of one cache page into an LDS tile. Tokens at
-// or beyond `nvalid` (past the end of the sequence) re-read token nvalid-1 so
-// the tile never holds stale or poisoned data; their weights are exactly 0.
-// Wave w copies the latent rows t = 16*m + 4*w + q (m, q in 0..3), so its 16
-// row copies use only 4 swizzle patterns (lane offsets lat_off[q]).
-__device__ __forceinline__ void load_tile(lds_char* tile, const char* ckv_page,
-                                          const char* kr_page, int nvalid, int w, int lane,
-                                          const uint32_t (&lat_off)[4]) {
-#pragma unroll
-  for (int m = 0; m < 4; ++m)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int t = 16 * m + 4 * w + q;
-      const int ts = min(t, nvalid - 1);
-      global_to_lds16(ckv_page + (uint32_t)(ts * 1024) + lat_off[q], tile + t * 1024);
-    }
-#pragma unroll
-  for (int m2 = 0; m2 < 2; ++m2) {
-    const int m = 2 * w + m2;
-    const int t = 8 * m + (lane >> 3);
-    const int ts = min(t, nvalid - 1);
-    const int j = (lane & 7) ^ swz_rope(t);
-    global_to_lds16(kr_page + ts * 128 + j * 16, tile + kLatBytes + m * 1024);
-  }
+// Workgroup barrier that orders LDS traffic only: this wave's LDS operations
+// complete (lgkmcnt 0), then all waves meet. In-flight page copies (vmcnt)
+// keep running across it. The memory clobber keeps the compiler from moving
+// memory accesses across the barrier.
+__device__ __forceinline__ void lds_sync() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-__device__ void write_uniform_result(const DecodeParams& p, int b, int k, int g, float mval,
-                                     float lval, float uval) {
-  // Every row of the unit gets (m, l, U) = (mval, lval, uval); used to mark
-  // out-of-range sequences with NaN.
+// Wait until at most N of this wave's page copies are in flight (copies
+// complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_copies() {
+  static_assert(N >= 0 && N <= 15, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
+// One asynchronous 16-byte-per-lane global -> LDS copy: lane i's 16 bytes
+// from page + voff land at LDS byte address lds + 16*i. Written as inline
+// assembly so the compiler's wait insertion never serializes it with later
+// LDS traffic; the issuing wave waits for it explicitly (wait_copies) before
+// the barrier that publishes the tile. It has no output registers, and its
+// address operands are consumed at issue. m0 (the LDS base register of the
+// copy) is restored afterwards.
+__device__ __forceinline__ void dma16(const void* page, uint32_t voff, const lds_char* lds) {
+  const uint32_t lds_addr = (uint32_t)(uintptr_t)lds;
+  uint32_t saved_m0;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved_m0)
+      : "s"(lds_addr), "v"(voff), "s"(page)
+      : "memory");
+}
+
+__device__ void write_uniform_result(const DecodeParams& p, int b, int k, int g, float v) {
+  // Every row of the unit gets (m, l, U) = (v, v, v); marks out-of-range
+  // sequences with NaN.
   const int tid = threadIdx.x;
   const int r0 = g * kRowsPerGroup;
   const int nrows = min(kRowsPerGroup, p.R - r0);
@@ -98,27 +119,27 @@ __device__ void write_uniform_result(const DecodeParams& p, int b, int k, int g,
     const int r = r0 + e / kDc, d = e % kDc;
     if (p.n_split == 1) {
       const size_t o = ((size_t)b * p.R + r) * kDc + d;
-      if (p.out_bf16) ((uint16_t*)p.out)[o] = f2bf(uval / lval);
-      else ((float*)p.out)[o] = uval / lval;
+      if (p.out_bf16) ((uint16_t*)p.out)[o] = f2bf(v);
+      else ((float*)p.out)[o] = v;
     } else {
-      p.part_u[(((size_t)b * p.n_split + k) * p.R + r) * kDc + d] = uval;
+      p.part_u[(((size_t)b * p.n_split + k) * p.R + r) * kDc + d] = v;
     }
   }
   for (int r = r0 + tid; r < r0 + nrows; r += kThreads) {
     if (p.n_split == 1) {
-      if (p.lse) p.lse[(size_t)b * p.R + r] = (mval + log2f(lval)) * kLn2;
+      if (p.lse) p.lse[(size_t)b * p.R + r] = v;
     } else {
       float* ml = p.part_ml + (((size_t)b * p.n_split + k) * p.R + r) * 2;
-      ml[0] = mval;
-      ml[1] = lval;
+      ml[0] = v;
+      ml[1] = v;
     }
   }
 }
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_mfma_bf16_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) char smem_raw[kLdsBytes];
-  lds_char* smem = (lds_char*)smem_raw;
+  lds_char* const smem = (lds_char*)smem_raw;
 
   const int bid = blockIdx.x;
   const int unit = (bid % kNumXcd) * p.per_xcd + bid / kNumXcd;
@@ -131,226 +152,301 @@ void decode_mfma_bf16_kernel(DecodeParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
-  const int hh = w & 1;     // score rows 32*hh..+31 of the group
-  const int th = w >> 1;    // score tokens 32*th..+31 of each page
   const int i16 = lane & 15;
   const int G4 = lane >> 4;
 
-  // ---- sequence and split bounds, range checks -----------------------------
+  const int row0 = g * kRowsPerGroup;
   const int L = p.seq_lens[b];
-  bool bad = (L < p.T) || (L > p.max_seq_len) || ((L + kPage - 1) / kPage > p.max_pages);
   const int tok0 = k * p.split_tokens;
   const int tok1 = min(tok0 + p.split_tokens, L);
   const int pg_begin = tok0 / kPage;
   const int pg_end = (tok1 + kPage - 1) / kPage;
-  const int32_t* btrow = p.block_table + (size_t)b * p.max_pages;
-  if (!bad) {
-    bool local_bad = false;
-    for (int j = pg_begin + tid; j < pg_end; j += kThreads) {
-      const int id = btrow[j];
-      local_bad |= (id < 0) || (id >= p.n_pages);
+  const int n_tiles = (tok1 - tok0 + kTileTok - 1) / kTileTok;
+  // sequence-level range checks; page ids are checked by the aggregation team
+  const bool seq_bad = (L < p.T) || (L > p.max_seq_len) ||
+                       ((L + kPage - 1) / kPage > p.max_pages) ||
+                       (pg_end - pg_begin) > kMaxSplitPages;
+  int* const ids = (int*)(smem_raw + kOffIds);
+  lds_char* const pbuf = smem + kOffP;
+  float* const alphabuf = (float*)(smem_raw + kOffAlpha);   // [2][64]
+  float* const redmax = (float*)(smem_raw + kOffRed);       // [2][64]
+  float* const lsum = (float*)(smem_raw + kOffLsum);        // [2][64]
+  float* const mbuf = (float*)(smem_raw + kOffM);           // [64]
+  const char* const ckv_base = (const char*)p.ckv;
+  const char* const kr_base = (const char*)p.kr;
+
+  // The two teams take fully separate code paths; both meet in the same
+  // sequence of workgroup barriers.
+  if (w < 4) {
+    // ======================= score team ======================================
+    const int hh = w & 1;    // rows 32*hh..+31
+    const int th = w >> 1;   // tokens 16*th..+15 of each tile
+    // absorbed queries of this wave's rows, loaded while the aggregation team
+    // checks the block table
+    bf16x8_t qB[2][18];
+    const bool active = !seq_bad && tok0 < tok1;
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) {
+      const int r = row0 + 32 * hh + 16 * ht + i16;
+      if (active && r < p.R) {
+        const uint16_t* ql = (const uint16_t*)p.q_lat + ((size_t)b * p.R + r) * kDc + 8 * G4;
+        const uint16_t* qr = (const uint16_t*)p.q_rope + ((size_t)b * p.R + r) * kDr + 8 * G4;
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks) qB[ht][ks] = load_bf16x8(ql + 32 * ks);
+        qB[ht][16] = load_bf16x8(qr);
+        qB[ht][17] = load_bf16x8(qr + 32);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < 18; ++ks) qB[ht][ks] = (bf16x8_t){0, 0, 0, 0, 0, 0, 0, 0};
+      }
     }
-    bad = __syncthreads_or(local_bad);
-  }
-  if (bad) {
-    write_uniform_result(p, b, k, g, __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""));
+    if (seq_bad || __syncthreads_or(false)) {
+      write_uniform_result(p, b, k, g, __builtin_nanf(""));
+      return;
+    }
+    if (tok0 >= tok1) return;   // split past the end of the sequence: no partial
+    // visible-token limit of a row: s < min(L - T + t + 1, tok1)
+    auto row_limit = [&](int rr) __attribute__((always_inline)) -> int {
+      const int r = row0 + rr;
+      const int t = (r < p.R) ? r / p.H : 0;
+      return min(L - p.T + t + 1, tok1);
+    };
+    const int lim_min = row_limit(0);   // the group's first (earliest) query token
+    int lim_s[2];
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) lim_s[ht] = row_limit(32 * hh + 16 * ht + i16);
+    const int fl = swz_lat(i16);     // token & 15 == i16 for this lane's A rows
+    const int fr = i16 >> 1;         // rope swizzle of this lane's A rows
+    float m_s[2] = {-INFINITY, -INFINITY};
+    float l_s[2] = {0.f, 0.f};
+
+    for (int j = 0; j <= n_tiles; ++j) {
+      lds_sync();  // (X) tile j resident
+      f32x4_t S[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+      const int stok0 = tok0 + j * kTileTok;   // first token of tile j
+      if (j < n_tiles) {
+        lds_char* const tile = smem + (j % kNumBuf) * kTileBytes;
+        const lds_char* const lat0 = tile + (16 * th + i16) * 1024;
+        const lds_char* const rope0 = tile + kLatTile + (16 * th + i16) * 128;
+        auto frag = [&](int ks) __attribute__((always_inline)) -> bf16x8_t {
+          if (ks < 16)
+            return lds_read_b128(lat0 + (16 * (ks >> 2) + ((4 * (ks & 3) + G4) ^ fl)) * 16);
+          return lds_read_b128(rope0 + ((4 * (ks - 16) + G4) ^ fr) * 16);
+        };
+        constexpr int kRing = 6;
+        bf16x8_t ring[kRing];
+#pragma unroll
+        for (int f = 0; f < kRing; ++f) ring[f] = frag(f);
+        __builtin_amdgcn_sched_group_barrier(0x100, kRing, 0);
+#pragma unroll
+        for (int f = 0; f < 18; ++f) {
+          const bf16x8_t a = ring[f % kRing];
+          if (f + kRing < 18) ring[f % kRing] = frag(f + kRing);
+          S[0] = mfma16x16x32(a, qB[0][f], S[0]);
+          S[1] = mfma16x16x32(a, qB[1][f], S[1]);
+          if (f + kRing < 18) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        }
+        // scale, mask, tile maxima of this wave's rows
+        const bool masked = stok0 + kTileTok > lim_min;
+        float mx[2] = {-INFINITY, -INFINITY};
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float z = S[ht][i] * p.scale_log2;
+            if (masked && stok0 + 16 * th + 4 * G4 + i >= lim_s[ht]) z = -INFINITY;
+            S[ht][i] = z;
+            mx[ht] = fmaxf(mx[ht], z);
+          }
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht) {
+          mx[ht] = wave_max16(mx[ht]);
+          if (lane < 16) redmax[th * 64 + 32 * hh + 16 * ht + lane] = mx[ht];
+        }
+      }
+      lds_sync();  // (Y) tile maxima of all rows visible
+      if (j < n_tiles) {
+        lds_char* const pj = pbuf + (j & 1) * kPBytes;
+        float* const aj = alphabuf + (j & 1) * 64;
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht) {
+          const int rr = 32 * hh + 16 * ht + i16;
+          const float mt = fmaxf(redmax[rr], redmax[64 + rr]);
+          const float mold = m_s[ht];
+          const float mnew = (mt - mold > kLazyMax) ? mt : mold;   // -inf - -inf is NaN: keep
+          const float base = (mnew == -INFINITY) ? 0.f : mnew;
+          const float alpha = (mnew == mold) ? 1.f : fast_exp2(mold - mnew);
+          m_s[ht] = mnew;
+          if (th == 0 && lane < 16) aj[rr] = alpha;
+          const uint32_t lo = pack_bf16x2(fast_exp2(S[ht][0] - base), fast_exp2(S[ht][1] - base));
+          const uint32_t hi = pack_bf16x2(fast_exp2(S[ht][2] - base), fast_exp2(S[ht][3] - base));
+          const float ls = bf2f(lo & 0xffff) + bf2f(lo >> 16) + bf2f(hi & 0xffff) + bf2f(hi >> 16);
+          *(MLA_LDS u32x2_t*)(pj + rr * kPStride + (16 * th + 4 * G4) * 2) = (u32x2_t){lo, hi};
+          l_s[ht] = l_s[ht] * alpha + wave_sum16(ls);
+        }
+      }
+    }
+    if (lane < 16) {
+      lsum[th * 64 + 32 * hh + lane] = l_s[0];
+      lsum[th * 64 + 32 * hh + 16 + lane] = l_s[1];
+      if (th == 0) {
+        mbuf[32 * hh + lane] = m_s[0];
+        mbuf[32 * hh + 16 + lane] = m_s[1];
+      }
+    }
+    lds_sync();  // (Z) row sums and reference maxima published
     return;
   }
-  if (tok0 >= tok1) return;   // split past the end of the sequence: no partial
 
-  const int row0 = g * kRowsPerGroup;
-  // visible-token limit of a row: s < min(L - T + t + 1, tok1)
-  auto row_limit = [&](int rr) -> int {
-    const int r = row0 + rr;
-    const int t = (r < p.R) ? r / p.H : 0;
-    return min(L - p.T + t + 1, tok1);
-  };
-  // smallest limit over the group's rows (the first query token's rows)
-  const int lim_min = row_limit(0);
-
-  // ---- absorbed queries of this wave's 32 rows in registers -----------------
-  bf16x8_t qB[2][18];
-  int lim_s[2];
-#pragma unroll
-  for (int ht = 0; ht < 2; ++ht) {
-    const int rr = 32 * hh + 16 * ht + i16;
-    const int r = row0 + rr;
-    lim_s[ht] = row_limit(rr);
-    if (r < p.R) {
-      const uint16_t* ql = (const uint16_t*)p.q_lat + ((size_t)b * p.R + r) * kDc + 8 * G4;
-      const uint16_t* qr = (const uint16_t*)p.q_rope + ((size_t)b * p.R + r) * kDr + 8 * G4;
-#pragma unroll
-      for (int ks = 0; ks < 16; ++ks) qB[ht][ks] = load_bf16x8(ql + 32 * ks);
-      qB[ht][16] = load_bf16x8(qr);
-      qB[ht][17] = load_bf16x8(qr + 32);
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < 18; ++ks) qB[ht][ks] = (bf16x8_t){0, 0, 0, 0, 0, 0, 0, 0};
+  // ========================= aggregation team ===============================
+  {
+    bool local_bad = false;
+    if (!seq_bad) {
+      const int32_t* btrow = p.block_table + (size_t)b * p.max_pages;
+      for (int j = pg_begin + (tid - 256); j < pg_end; j += 256) {
+        const int id = btrow[j];
+        local_bad |= (id < 0) || (id >= p.n_pages);
+        ids[j - pg_begin] = id;
+      }
+    }
+    if (seq_bad || __syncthreads_or(local_bad)) {
+      write_uniform_result(p, b, k, g, __builtin_nanf(""));
+      return;
     }
   }
-
-  lds_char* const pbuf = smem + kOffP;
-  float* const redmax = (float*)(smem_raw + kOffRed);   // [2][64]
-  float* const lsum = (float*)(smem_raw + kOffLsum);    // [2][64]
-  float* const alphabuf = (float*)(smem_raw + kOffAlpha);
-  float* const mbuf = (float*)(smem_raw + kOffM);
+  if (tok0 >= tok1) return;   // split past the end of the sequence: no partial
+  const int v = w - 4;           // latent dims 128*v..+127
+  // copy duties: latent rows t = 4*m + v (m = 0..7) and rope block v of each tile;
+  // the rows' swizzle class (t & 15) cycles through 4 values
   uint32_t lat_off[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) lat_off[q] = (uint32_t)(lane ^ swz_lat(4 * w + q)) * 16u;
-
-  // per-lane swizzle constants
-  const int fl = swz_lat(i16);            // score rows: token & 15 == i16
-  const int fr = i16 >> 1;                // rope swizzle of score rows
-  const int xq = 4 * (G4 & 1) + (i16 >> 2);
-  const int c0 = (i16 & 3) >> 1;
+  for (int q = 0; q < 4; ++q) lat_off[q] = (uint32_t)(lane ^ swz_lat((4 * q + v) & 15)) * 16u;
+  // source of tile jt: its LDS buffer, page pointers and the last valid slot
+  struct TileSrc {
+    lds_char* tile;
+    const char* cp;
+    const char* rp;
+    int base_t, last;
+  };
+  auto tile_src = [&](int jt) __attribute__((always_inline)) -> TileSrc {
+    const int t0 = tok0 + jt * kTileTok;            // first token of the tile
+    const int id = __builtin_amdgcn_readfirstlane(ids[(t0 - tok0) / kPage]);
+    const int base_t = t0 % kPage;                  // 0 or 32 within the page
+    return TileSrc{smem + (jt % kNumBuf) * kTileBytes,
+                   ckv_base + (size_t)id * (kPage * kDc * 2),
+                   kr_base + (size_t)id * (kPage * kDr * 2), base_t,
+                   L - 1 - (t0 - base_t)};          // last valid token's page slot
+  };
+  // copy op (0..8) of this wave for a tile: latent rows t = 4*op + v, then the
+  // rope block v
+  auto dma_op = [&](const TileSrc& src, int op) __attribute__((always_inline)) {
+    if (op < 8) {
+      const int t = 4 * op + v;
+      const int ts = min(src.base_t + t, src.last);
+      dma16(src.cp, (uint32_t)(ts * 1024) + lat_off[op & 3], src.tile + t * 1024);
+    } else {
+      const int t = 8 * v + (lane >> 3);
+      const int ts = min(src.base_t + t, src.last);
+      const int jc = (lane & 7) ^ swz_rope(t);
+      dma16(src.rp, (uint32_t)(ts * 128 + jc * 16), src.tile + kLatTile + v * 1024);
+    }
+  };
+  auto issue_tile = [&](int jt) __attribute__((always_inline)) {
+    const TileSrc src = tile_src(jt);
+#pragma unroll
+    for (int op = 0; op < kDmaPerWave; ++op) dma_op(src, op);
+  };
 
   f32x4_t U[4][8];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) U[rt][dt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-  float m_s[2] = {-INFINITY, -INFINITY};
-  float l_s[2] = {0.f, 0.f};
+  const int xq32 = 32 * (4 * (G4 & 1) + (i16 >> 2));
+  const int c0 = (i16 & 3) >> 1;
 
-  const char* ckv_base = (const char*)p.ckv;
-  const char* kr_base = (const char*)p.kr;
-  {
-    const int id = __builtin_amdgcn_readfirstlane(btrow[pg_begin]);
-    load_tile(smem, ckv_base + (size_t)id * kLatBytes, kr_base + (size_t)id * kRopeBytes,
-              min(kPage, L - pg_begin * kPage), w, lane, lat_off);
+  issue_tile(0);
+  if (n_tiles > 1) {
+    issue_tile(1);
+    wait_copies<kDmaPerWave>();
+  } else {
+    wait_copies<0>();
   }
-  // page id of the next page, fetched one iteration ahead of its use
-  int id_next = (pg_begin + 1 < pg_end) ? btrow[pg_begin + 1] : 0;
 
-  for (int pg = pg_begin; pg < pg_end; ++pg) {
-    lds_char* const tile = smem + ((pg - pg_begin) & 1) * kTileBytes;
-    wait_vmem();
-    block_sync();  // (A) tile pg resident; previous page fully consumed
-    if (pg + 1 < pg_end) {
-      const int id = __builtin_amdgcn_readfirstlane(id_next);
-      load_tile(smem + ((pg + 1 - pg_begin) & 1) * kTileBytes, ckv_base + (size_t)id * kLatBytes,
-                kr_base + (size_t)id * kRopeBytes, min(kPage, L - (pg + 1) * kPage), w, lane,
-                lat_off);
-      if (pg + 2 < pg_end) id_next = btrow[pg + 2];
-    }
-
-    // ---- 1. scores: tokens 32*th + 16*tt + (4*G4 + i), rows 32*hh + 16*ht + i16
-    f32x4_t S[2][2];
+  bf16x8_t pa[4];
+  // half 0 issues copy ops 0..4 of the next-but-one tile between its MFMA
+  // groups, half 1 ops 5..8 (when `more`)
+  auto pv_half = [&](const lds_char* tile, int half, bool more, const TileSrc& src) __attribute__((always_inline)) {
+    const lds_char* const rowA = tile + (8 * G4 + (i16 >> 2)) * 1024 + 256 * v + (i16 & 1) * 8;
+    auto bfrag = [&](int dt) __attribute__((always_inline)) -> bf16x8_t {
+      const int dx = (32 * dt) ^ xq32;              // 32 * (dt ^ xq)
+      const bf16x4_t lo = lds_read_tr16(rowA + dx + 16 * c0);                  // tokens +0..3
+      const bf16x4_t hi = lds_read_tr16(rowA + 4 * 1024 + dx + 16 * (c0 ^ 1)); // tokens +4..7
+      return concat(lo, hi);
+    };
+    constexpr int kRingB = 2;
+    bf16x8_t ringb[kRingB];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      S[tt][0] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-      S[tt][1] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-      const int t = 32 * th + 16 * tt + i16;
-      const lds_char* latp = tile + t * 1024;
+    for (int e = 0; e < kRingB; ++e) ringb[e] = bfrag(4 * half + e);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kRingB, 0);
 #pragma unroll
-      for (int ks = 0; ks < 16; ++ks) {
-        const bf16x8_t a = lds_read_b128(latp + (16 * (ks >> 2) + ((4 * (ks & 3) + G4) ^ fl)) * 16);
-        S[tt][0] = mfma16x16x32(a, qB[0][ks], S[tt][0]);
-        S[tt][1] = mfma16x16x32(a, qB[1][ks], S[tt][1]);
-      }
-      const lds_char* ropep = tile + kLatBytes + t * 128;
+    for (int e = 0; e < 4; ++e) {
+      const int dt = 4 * half + e;
+      const bf16x8_t bv = ringb[e % kRingB];
+      if (e + kRingB < 4) ringb[e % kRingB] = bfrag(dt + kRingB);
 #pragma unroll
-      for (int ks = 16; ks < 18; ++ks) {
-        const bf16x8_t a = lds_read_b128(ropep + ((4 * (ks - 16) + G4) ^ fr) * 16);
-        S[tt][0] = mfma16x16x32(a, qB[0][ks], S[tt][0]);
-        S[tt][1] = mfma16x16x32(a, qB[1][ks], S[tt][1]);
-      }
-    }
-
-    const int ptok0 = pg * kPage;
-    const bool masked = ptok0 + kPage > lim_min;
-    float mx[2] = {-INFINITY, -INFINITY};
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int ht = 0; ht < 2; ++ht)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float z = S[tt][ht][i] * p.scale_log2;
-          if (masked) {
-            const int s = ptok0 + 32 * th + 16 * tt + 4 * G4 + i;
-            if (s >= lim_s[ht]) z = -INFINITY;
-          }
-          S[tt][ht][i] = z;
-          mx[ht] = fmaxf(mx[ht], z);
+      for (int rt = 0; rt < 4; ++rt) U[rt][dt] = mfma16x16x32(pa[rt], bv, U[rt][dt]);
+      if (e + kRingB < 4) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      if (more) {
+        if (half == 0) {
+          dma_op(src, e == 0 ? 0 : e + 1);
+          if (e == 0) dma_op(src, 1);
+        } else if (e < 3) {
+          dma_op(src, 5 + e);
+          if (e == 2) dma_op(src, 8);
         }
-#pragma unroll
-    for (int ht = 0; ht < 2; ++ht) {
-      mx[ht] = wave_max16(mx[ht]);
-      if (lane < 16) redmax[th * 64 + 32 * hh + 16 * ht + lane] = mx[ht];
-    }
-    block_sync();  // (B) page maxima of all rows visible
-
-    // ---- 2. softmax: probabilities of this wave's 32 tokens x 32 rows -------
-#pragma unroll
-    for (int ht = 0; ht < 2; ++ht) {
-      const int rr = 32 * hh + 16 * ht + i16;
-      const float mt = fmaxf(redmax[rr], redmax[64 + rr]);
-      const float mold = m_s[ht];
-      const float mnew = (mt - mold > kLazyMax) ? mt : mold;   // -inf - -inf is NaN: keep
-      const float base = (mnew == -INFINITY) ? 0.f : mnew;
-      const float alpha = (mnew == mold) ? 1.f : fast_exp2(mold - mnew);
-      m_s[ht] = mnew;
-      if (th == 0 && lane < 16) alphabuf[rr] = alpha;
-      float ls = 0.f;
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const uint32_t lo = pack_bf16x2(fast_exp2(S[tt][ht][0] - base), fast_exp2(S[tt][ht][1] - base));
-        const uint32_t hi = pack_bf16x2(fast_exp2(S[tt][ht][2] - base), fast_exp2(S[tt][ht][3] - base));
-        ls += bf2f(lo & 0xffff) + bf2f(lo >> 16) + bf2f(hi & 0xffff) + bf2f(hi >> 16);
-        *(MLA_LDS u32x2_t*)(pbuf + rr * kPStride + (32 * th + 16 * tt + 4 * G4) * 2) =
-            (u32x2_t){lo, hi};
       }
-      l_s[ht] = l_s[ht] * alpha + wave_sum16(ls);
     }
-    block_sync();  // (C) probability tile and rescale factors complete
+  };
 
-    // ---- 3. aggregation: rows 16*rt + (4*G4 + i), dims 128*w + 16*dt + i16 --
-    {
-      f32x4_t al[4];
+  for (int j = 0; j <= n_tiles; ++j) {
+    lds_sync();  // (X) tile j resident; P(j-1) and alpha(j-1) published
+    const bool more = j + 2 < n_tiles;
+    const TileSrc src = tile_src(more ? j + 2 : 0);
+    if (more && j == 0) issue_tile(j + 2);
+    const lds_char* const tile = smem + ((j + kNumBuf - 1) % kNumBuf) * kTileBytes;   // tile j-1
+    if (j >= 1) {
+      const lds_char* const pj = pbuf + ((j - 1) & 1) * kPBytes;
+      const float* const aj = alphabuf + ((j - 1) & 1) * 64;
       bool rescale = false;
+      f32x4_t al[4];
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
-        al[rt] = *(const f32x4_t*)(alphabuf + 16 * rt + 4 * G4);
+        al[rt] = *(const f32x4_t*)(aj + 16 * rt + 4 * G4);
         rescale |= (al[rt][0] != 1.f) | (al[rt][1] != 1.f) | (al[rt][2] != 1.f) | (al[rt][3] != 1.f);
       }
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+        pa[rt] = lds_read_b128(pj + (16 * rt + i16) * kPStride + 16 * G4);
       if (__builtin_amdgcn_ballot_w64(rescale)) {
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
           for (int dt = 0; dt < 8; ++dt) U[rt][dt] *= al[rt];
       }
+      pv_half(tile, 0, more, src);
     }
-    const int xq32 = 32 * xq;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8_t a[4];
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
-        a[rt] = lds_read_b128(pbuf + (16 * rt + i16) * kPStride + (32 * ks + 8 * G4) * 2);
-      const lds_char* rowA = tile + (32 * ks + 8 * G4 + (i16 >> 2)) * 1024 + 256 * w + (i16 & 1) * 8;
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const int dx = (32 * dt) ^ xq32;              // 32 * (dt ^ xq)
-        const bf16x4_t lo = lds_read_tr16(rowA + dx + 16 * c0);                  // tokens +0..3
-        const bf16x4_t hi = lds_read_tr16(rowA + 4 * 1024 + dx + 16 * (c0 ^ 1)); // tokens +4..7
-        const bf16x8_t bv = concat(lo, hi);
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) U[rt][dt] = mfma16x16x32(a[rt], bv, U[rt][dt]);
-      }
-    }
+    lds_sync();  // (Y)
+    if (j >= 1) pv_half(tile, 1, more, src);
+    // tile j+1 must be resident at the next (X); tile j+2's copies may fly on
+    if (more) wait_copies<kDmaPerWave>();
+    else wait_copies<0>();
   }
+  lds_sync();  // (Z) row sums and reference maxima published
 
-  // ---- finish: total row sums, then u = U / l or fp32 partials ------------
-  if (lane < 16) {
-    lsum[th * 64 + 32 * hh + lane] = l_s[0];
-    lsum[th * 64 + 32 * hh + 16 + lane] = l_s[1];
-    if (th == 0) {
-      mbuf[32 * hh + lane] = m_s[0];
-      mbuf[32 * hh + 16 + lane] = m_s[1];
-    }
-  }
-  block_sync();
+  // ---- finish: u = U / l or fp32 partials ----------------------------------
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
@@ -361,20 +457,20 @@ void decode_mfma_bf16_kernel(DecodeParams p) {
       const float lval = lsum[rr] + lsum[64 + rr];
       const float mval = mbuf[rr];
       if (p.n_split == 1) {
-        const size_t o = ((size_t)b * p.R + r) * kDc + 128 * w + i16;
+        const size_t o = ((size_t)b * p.R + r) * kDc + 128 * v + i16;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
           const float u = U[rt][dt][i] / lval;
           if (p.out_bf16) ((uint16_t*)p.out)[o + 16 * dt] = f2bf(u);
           else ((float*)p.out)[o + 16 * dt] = u;
         }
-        if (p.lse && w == 0 && i16 == 0) p.lse[(size_t)b * p.R + r] = (mval + log2f(lval)) * kLn2;
+        if (p.lse && v == 0 && i16 == 0) p.lse[(size_t)b * p.R + r] = (mval + log2f(lval)) * kLn2;
       } else {
         const size_t base = ((size_t)b * p.n_split + k) * p.R + r;
-        float* pu = p.part_u + base * kDc + 128 * w + i16;
+        float* pu = p.part_u + base * kDc + 128 * v + i16;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) pu[16 * dt] = U[rt][dt][i];
-        if (w == 0 && i16 == 0) {
+        if (v == 0 && i16 == 0) {
           p.part_ml[base * 2] = mval;
           p.part_ml[base * 2 + 1] = lval;
         }

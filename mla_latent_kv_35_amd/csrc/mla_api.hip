@@ -36,6 +36,7 @@ int check_shape(const mla_decode_args* a) {
   if (a->max_seq_len < a->T || (int64_t)a->max_seq_len > (int64_t)a->max_pages_per_seq * kPage)
     return MLA_ERR_SHAPE;
   if (a->split_tokens < 0 || a->split_tokens % kPage != 0) return MLA_ERR_SHAPE;
+  if (a->split_tokens > kMaxSplitPages * kPage) return MLA_ERR_UNSUPPORTED;
   if (a->total_tokens < 0) return MLA_ERR_SHAPE;
   if (!(a->softmax_scale > 0.f) || !isfinite(a->softmax_scale)) return MLA_ERR_SHAPE;
   if ((int64_t)a->T * a->H > (1 << 20)) return MLA_ERR_UNSUPPORTED;
@@ -75,6 +76,7 @@ Plan make_plan(const mla_decode_args* a) {
     int64_t unit_pages = (pl.G * pages_total + target - 1) / target;
     unit_pages = std::max<int64_t>(unit_pages, 4);
     unit_pages = std::min<int64_t>(unit_pages, max_pages);
+    unit_pages = std::min<int64_t>(unit_pages, kMaxSplitPages);
     pl.split_tokens = (int)(unit_pages * kPage);
   }
   pl.n_split = (int)((Lmax + pl.split_tokens - 1) / pl.split_tokens);

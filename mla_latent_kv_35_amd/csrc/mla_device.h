@@ -69,17 +69,24 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70 
 // which is immaterial for softmax weights next to the row maximum's 2^0).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Reductions across the four 16-lane rows of a wave (lanes l, l^16, l^32,
+// l^48) on the VALU: v_permlane16_swap exchanges odd rows of its first operand
+// with even rows of its second, v_permlane32_swap the upper half of the first
+// with the lower half of the second; with both operands equal, the pair
+// {result0, result1} holds {v[l], v[l^16]} (resp. {v[l], v[l^32]}) up to order.
+// Every lane ends with the same bits: (r0 op r1) op (r2 op r3).
 __device__ __forceinline__ float wave_max16(float v) {
-  // reduce across the four 16-lane groups (lanes l, l^16, l^32, l^48)
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 __device__ __forceinline__ float wave_sum16(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float m = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 }  // namespace mla

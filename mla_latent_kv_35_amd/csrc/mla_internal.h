@@ -15,6 +15,7 @@ constexpr int kDc = 512;
 constexpr int kDr = 64;
 constexpr int kDh = 128;
 constexpr int kRowsPerGroup = 64;   // query rows per decode workgroup (MFMA kernel)
+constexpr int kMaxSplitPages = 1024; // pages of one split (MFMA kernel keeps their ids in LDS)
 constexpr int kNumXcd = 8;          // MI355X: 8 XCDs, workgroups dispatched round-robin
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
