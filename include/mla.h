@@ -153,9 +153,11 @@ int mla_decode_plan(const mla_decode_args* args, int* split_tokens, int* n_split
  *   u    = sum_s a_s c_s            (latent-space aggregate, W^UV not applied)
  *   lse  = ln sum_s exp(z_s)
  * F32 caches run an fp32 kernel; BF16 caches run bf16 MFMA with fp32 softmax
- * and accumulation; FP8_E4M3 latents run fp8 MFMA for the latent scores
- * (q_lat quantized per row after absorption) and bf16 MFMA for rope and
- * aggregation, scales applied in fp32.
+ * and accumulation; FP8_E4M3 latents stay fp8 in HBM and LDS and are widened
+ * exactly to bf16 in registers for bf16 MFMA (q_lat is not quantized), the
+ * per-token scale applied in fp32 to the latent score and to the weight:
+ *   z_s = (scale_s * (q_lat . code_s) + q_rope . k^R_s) * softmax_scale
+ *   u   = sum_s (a_s * scale_s) code_s
  */
 int mla_decode_paged(const mla_decode_args* args, void* stream);
 

@@ -1,9 +1,10 @@
-// Paged absorbed-MLA decode on gfx950 bf16 MFMA.
+// Paged absorbed-MLA decode on gfx950 MFMA, for bf16 caches and for fp8
+// (OCP E4M3FN) latent caches with one fp32 scale per token.
 //
 // One workgroup owns a work unit (sequence b, split k, group g of 64 query
 // rows) and streams the split's cache through LDS in tiles of 32 tokens
-// (half a page): 512 latent + 64 rope bf16 per token, the 576-element cache
-// of PaperTrace "02 · DeepSeek-V2 analysis", section 1.3.
+// (half a page): 512 latent + 64 rope elements per token, the 576-element
+// cache of PaperTrace "02 · DeepSeek-V2 analysis", section 1.3.
 //
 // The workgroup's 8 waves form two teams that work one tile apart, so that on
 // every SIMD one wave's softmax and LDS traffic overlap the other wave's MFMAs:
@@ -26,6 +27,15 @@
 // while two are in use. All barriers order LDS only; the page copies are
 // waited for explicitly with vmcnt by the waves that issued them.
 //
+// fp8 latent caches: tiles stay fp8 in LDS (half the bytes of bf16); every
+// E4M3FN code is widened exactly to bf16 in registers right before its MFMA,
+// so the cache's own rounding is the only quantization on the path (the
+// absorbed query stays bf16: quantizing it to fp8 per row would add an error
+// of about 5 % of the output on these workloads). The token scale multiplies
+// the latent score in fp32, z = scale_s * (q_lat . code_s) + q_rope . k^R_s,
+// and is folded into the probability for the aggregation, P' = p * scale_s,
+// which reads the codes transposed (ds_read_b64_tr_b8).
+//
 // The split ends by writing either u = U / l and lse, or fp32 partials
 // (m, l, U) for the log-sum-exp combine kernel.
 #include "mla_device.h"
@@ -36,23 +46,31 @@ namespace {
 
 constexpr int kThreads = 512;
 constexpr int kTileTok = 32;
-constexpr int kLatTile = kTileTok * 1024;           // 32768: latent rows of 1 KB
-constexpr int kRopeTile = kTileTok * 128;           // 4096: rope rows of 128 B
-constexpr int kTileBytes = kLatTile + kRopeTile;    // 36864
+constexpr int kRopeTile = kTileTok * 128;           // 4096: rope rows of 128 B (bf16)
 constexpr int kNumBuf = 4;
 constexpr int kPStride = 80;                        // bytes per probability row (32 bf16 + pad)
 constexpr int kPBytes = kRowsPerGroup * kPStride;   // 5120
-constexpr int kOffP = kNumBuf * kTileBytes;         // 147456: P[2]
-constexpr int kOffAlpha = kOffP + 2 * kPBytes;      // alpha[2][64] f32
-constexpr int kOffRed = kOffAlpha + 2 * 64 * 4;     // tile maxima [2][64] f32
-constexpr int kOffLsum = kOffRed + 2 * 64 * 4;      // row sums [2][64] f32
-constexpr int kOffM = kOffLsum + 2 * 64 * 4;        // final reference max [64] f32
-constexpr int kOffIds = kOffM + 64 * 4;             // page ids of the split
-constexpr int kLdsBytes = kOffIds + kMaxSplitPages * 4;   // 163584
-static_assert(kLdsBytes <= 163840, "LDS budget");
 
-// DMA copies per tile per aggregation wave: 8 latent rows + 1 rope block.
-constexpr int kDmaPerWave = 9;
+// LDS tile geometry: latent rows of 1 KB (bf16) or 512 B (fp8), then the rope
+// rows, then (fp8) the tile's 32 token scales in a 256-B slot.
+template <bool FP8>
+struct Geo {
+  static constexpr int kLatRow = FP8 ? 512 : 1024;
+  static constexpr int kLatTile = kTileTok * kLatRow;
+  static constexpr int kScaleOff = kLatTile + kRopeTile;
+  static constexpr int kTileBytes = kLatTile + kRopeTile + (FP8 ? 256 : 0);
+  static constexpr int kOffP = kNumBuf * kTileBytes;        // P[2]
+  static constexpr int kOffAlpha = kOffP + 2 * kPBytes;     // alpha[2][64] f32
+  static constexpr int kOffRed = kOffAlpha + 2 * 64 * 4;    // tile maxima [2][64] f32
+  static constexpr int kOffLsum = kOffRed + 2 * 64 * 4;     // row sums [2][64] f32
+  static constexpr int kOffM = kOffLsum + 2 * 64 * 4;       // final reference max [64] f32
+  static constexpr int kOffIds = kOffM + 64 * 4;            // page ids of the split
+  static constexpr int kLdsBytes = kOffIds + kMaxSplitPages * 4;
+  // page copies per tile per aggregation wave: bf16 8 latent rows + 1 rope
+  // block; fp8 4 latent row pairs + 1 rope block (+ the scales on wave 0)
+  static constexpr int kDma = FP8 ? 5 : 9;
+  static_assert(kLdsBytes <= 163840, "LDS budget");
+};
 
 // The running reference max of a row only moves when a tile's max exceeds it
 // by more than kLazyMax (log2 units): probabilities are then bounded by
@@ -109,6 +127,31 @@ __device__ __forceinline__ void dma16(const void* page, uint32_t voff, const lds
       : "memory");
 }
 
+// The same as dma16 with 4 bytes per lane (lane i's word lands at lds + 4*i).
+__device__ __forceinline__ void dma4(const void* base, uint32_t voff, const lds_char* lds) {
+  const uint32_t lds_addr = (uint32_t)(uintptr_t)lds;
+  uint32_t saved_m0;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved_m0)
+      : "s"(lds_addr), "v"(voff), "s"(base)
+      : "memory");
+}
+
+// 8 E4M3FN bytes -> 8 bf16 (exact: every E4M3FN value is a bf16 value).
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16(const i32x2_t& v) {
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  const bf2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], 1.0f, false);
+  const bf2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], 1.0f, true);
+  const bf2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[1], 1.0f, false);
+  const bf2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[1], 1.0f, true);
+  return (bf16x8_t){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
 __device__ void write_uniform_result(const DecodeParams& p, int b, int k, int g, float v) {
   // Every row of the unit gets (m, l, U) = (v, v, v); marks out-of-range
   // sequences with NaN.
@@ -136,9 +179,16 @@ __device__ void write_uniform_result(const DecodeParams& p, int b, int k, int g,
   }
 }
 
+template <bool FP8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void decode_mfma_bf16_kernel(DecodeParams p) {
-  __shared__ __attribute__((aligned(16))) char smem_raw[kLdsBytes];
+void decode_mfma_kernel(DecodeParams p) {
+  using Gm = Geo<FP8>;
+  constexpr int kLatRow = Gm::kLatRow;
+  constexpr int kLatTile = Gm::kLatTile;
+  constexpr int kTileBytes = Gm::kTileBytes;
+  constexpr int kOffP = Gm::kOffP, kOffAlpha = Gm::kOffAlpha, kOffRed = Gm::kOffRed;
+  constexpr int kOffLsum = Gm::kOffLsum, kOffM = Gm::kOffM, kOffIds = Gm::kOffIds;
+  __shared__ __attribute__((aligned(16))) char smem_raw[Gm::kLdsBytes];
   lds_char* const smem = (lds_char*)smem_raw;
 
   const int bid = blockIdx.x;
@@ -183,6 +233,7 @@ void decode_mfma_bf16_kernel(DecodeParams p) {
     const int th = w >> 1;   // tokens 16*th..+15 of each tile
     // absorbed queries of this wave's rows, loaded while the aggregation team
     // checks the block table
+    // query fragments: 16 latent k-steps + 2 rope k-steps per 16-row half
     bf16x8_t qB[2][18];
     const bool active = !seq_bad && tok0 < tok1;
 #pragma unroll
@@ -224,28 +275,68 @@ void decode_mfma_bf16_kernel(DecodeParams p) {
       lds_sync();  // (X) tile j resident
       f32x4_t S[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
       const int stok0 = tok0 + j * kTileTok;   // first token of tile j
+      f32x4_t tsc = {1.f, 1.f, 1.f, 1.f};       // fp8: scales of this lane's 4 tokens
       if (j < n_tiles) {
         lds_char* const tile = smem + (j % kNumBuf) * kTileBytes;
-        const lds_char* const lat0 = tile + (16 * th + i16) * 1024;
         const lds_char* const rope0 = tile + kLatTile + (16 * th + i16) * 128;
-        auto frag = [&](int ks) __attribute__((always_inline)) -> bf16x8_t {
-          if (ks < 16)
-            return lds_read_b128(lat0 + (16 * (ks >> 2) + ((4 * (ks & 3) + G4) ^ fl)) * 16);
-          return lds_read_b128(rope0 + ((4 * (ks - 16) + G4) ^ fr) * 16);
+        auto rfrag = [&](int ks) __attribute__((always_inline)) -> bf16x8_t {
+          return lds_read_b128(rope0 + ((4 * ks + G4) ^ fr) * 16);
         };
-        constexpr int kRing = 6;
-        bf16x8_t ring[kRing];
+        if constexpr (!FP8) {
+          const lds_char* const lat0 = tile + (16 * th + i16) * 1024;
+          auto frag = [&](int ks) __attribute__((always_inline)) -> bf16x8_t {
+            if (ks < 16)
+              return lds_read_b128(lat0 + (16 * (ks >> 2) + ((4 * (ks & 3) + G4) ^ fl)) * 16);
+            return rfrag(ks - 16);
+          };
+          constexpr int kRing = 6;
+          bf16x8_t ring[kRing];
 #pragma unroll
-        for (int f = 0; f < kRing; ++f) ring[f] = frag(f);
-        __builtin_amdgcn_sched_group_barrier(0x100, kRing, 0);
+          for (int f = 0; f < kRing; ++f) ring[f] = frag(f);
+          __builtin_amdgcn_sched_group_barrier(0x100, kRing, 0);
 #pragma unroll
-        for (int f = 0; f < 18; ++f) {
-          const bf16x8_t a = ring[f % kRing];
-          if (f + kRing < 18) ring[f % kRing] = frag(f + kRing);
-          S[0] = mfma16x16x32(a, qB[0][f], S[0]);
-          S[1] = mfma16x16x32(a, qB[1][f], S[1]);
-          if (f + kRing < 18) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          for (int f = 0; f < 18; ++f) {
+            const bf16x8_t a = ring[f % kRing];
+            if (f + kRing < 18) ring[f % kRing] = frag(f + kRing);
+            S[0] = mfma16x16x32(a, qB[0][f], S[0]);
+            S[1] = mfma16x16x32(a, qB[1][f], S[1]);
+            if (f + kRing < 18) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          }
+        } else {
+          // latent codes: 8 bytes per lane at 8-byte chunk (4*ks + G4) ^ (2*i16)
+          // of token row 16*th + i16, widened to bf16 before the MFMA
+          const lds_char* const lat0 = tile + (16 * th + i16) * 512;
+          auto frag8 = [&](int ks) __attribute__((always_inline)) -> i32x2_t {
+            return *(const MLA_LDS i32x2_t*)(lat0 + (((4 * ks + G4) ^ (2 * i16)) * 8));
+          };
+          constexpr int kRing = 6;
+          i32x2_t ring[kRing];
+#pragma unroll
+          for (int f = 0; f < kRing; ++f) ring[f] = frag8(f);
+          const bf16x8_t r0 = rfrag(0), r1 = rfrag(1);
+          __builtin_amdgcn_sched_group_barrier(0x100, kRing + 2, 0);
+          f32x4_t Sl[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+          for (int f = 0; f < 16; ++f) {
+            const bf16x8_t a = fp8x8_to_bf16(ring[f % kRing]);
+            if (f + kRing < 16) ring[f % kRing] = frag8(f + kRing);
+            Sl[0] = mfma16x16x32(a, qB[0][f], Sl[0]);
+            Sl[1] = mfma16x16x32(a, qB[1][f], Sl[1]);
+            if (f + kRing < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          }
+#pragma unroll
+          for (int ht = 0; ht < 2; ++ht) {
+            S[ht] = mfma16x16x32(r0, qB[ht][16], S[ht]);
+            S[ht] = mfma16x16x32(r1, qB[ht][17], S[ht]);
+          }
+          // token scales of this lane's 4 tokens on the latent part
+          tsc = *(const MLA_LDS f32x4_t*)(tile + Gm::kScaleOff + (16 * th + 4 * G4) * 4);
+#pragma unroll
+          for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S[ht][i] = fmaf(Sl[ht][i], tsc[i], S[ht][i]);
         }
         // scale, mask, tile maxima of this wave's rows
         const bool masked = stok0 + kTileTok > lim_min;
@@ -279,9 +370,19 @@ void decode_mfma_bf16_kernel(DecodeParams p) {
           const float alpha = (mnew == mold) ? 1.f : fast_exp2(mold - mnew);
           m_s[ht] = mnew;
           if (th == 0 && lane < 16) aj[rr] = alpha;
-          const uint32_t lo = pack_bf16x2(fast_exp2(S[ht][0] - base), fast_exp2(S[ht][1] - base));
-          const uint32_t hi = pack_bf16x2(fast_exp2(S[ht][2] - base), fast_exp2(S[ht][3] - base));
-          const float ls = bf2f(lo & 0xffff) + bf2f(lo >> 16) + bf2f(hi & 0xffff) + bf2f(hi >> 16);
+          const float e0 = fast_exp2(S[ht][0] - base), e1 = fast_exp2(S[ht][1] - base);
+          const float e2 = fast_exp2(S[ht][2] - base), e3 = fast_exp2(S[ht][3] - base);
+          uint32_t lo, hi;
+          float ls;
+          if constexpr (!FP8) {
+            lo = pack_bf16x2(e0, e1);
+            hi = pack_bf16x2(e2, e3);
+            ls = bf2f(lo & 0xffff) + bf2f(lo >> 16) + bf2f(hi & 0xffff) + bf2f(hi >> 16);
+          } else {
+            lo = pack_bf16x2(e0 * tsc[0], e1 * tsc[1]);
+            hi = pack_bf16x2(e2 * tsc[2], e3 * tsc[3]);
+            ls = (e0 + e1) + (e2 + e3);
+          }
           *(MLA_LDS u32x2_t*)(pj + rr * kPStride + (16 * th + 4 * G4) * 2) = (u32x2_t){lo, hi};
           l_s[ht] = l_s[ht] * alpha + wave_sum16(ls);
         }
@@ -317,8 +418,10 @@ void decode_mfma_bf16_kernel(DecodeParams p) {
   }
   if (tok0 >= tok1) return;   // split past the end of the sequence: no partial
   const int v = w - 4;           // latent dims 128*v..+127
-  // copy duties: latent rows t = 4*m + v (m = 0..7) and rope block v of each tile;
-  // the rows' swizzle class (t & 15) cycles through 4 values
+  // copy duties per tile: bf16 latent rows t = 4*op + v (op = 0..7); fp8
+  // latent row pairs (2q, 2q+1) with q = 4*op + v (op = 0..3); then rope
+  // block v; fp8 wave 0 also copies the 32 token scales.
+  const int n_ops = FP8 ? (v == 0 ? 6 : 5) : 9;
   uint32_t lat_off[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) lat_off[q] = (uint32_t)(lane ^ swz_lat((4 * q + v) & 15)) * 16u;
@@ -327,6 +430,7 @@ void decode_mfma_bf16_kernel(DecodeParams p) {
     lds_char* tile;
     const char* cp;
     const char* rp;
+    const char* sp;
     int base_t, last;
   };
   auto tile_src = [&](int jt) __attribute__((always_inline)) -> TileSrc {
@@ -334,28 +438,47 @@ void decode_mfma_bf16_kernel(DecodeParams p) {
     const int id = __builtin_amdgcn_readfirstlane(ids[(t0 - tok0) / kPage]);
     const int base_t = t0 % kPage;                  // 0 or 32 within the page
     return TileSrc{smem + (jt % kNumBuf) * kTileBytes,
-                   ckv_base + (size_t)id * (kPage * kDc * 2),
-                   kr_base + (size_t)id * (kPage * kDr * 2), base_t,
+                   ckv_base + (size_t)id * (kPage * kLatRow),
+                   kr_base + (size_t)id * (kPage * kDr * 2),
+                   FP8 ? (const char*)p.ckv_scale + (size_t)id * (kPage * 4) : nullptr, base_t,
                    L - 1 - (t0 - base_t)};          // last valid token's page slot
   };
-  // copy op (0..8) of this wave for a tile: latent rows t = 4*op + v, then the
-  // rope block v
   auto dma_op = [&](const TileSrc& src, int op) __attribute__((always_inline)) {
-    if (op < 8) {
-      const int t = 4 * op + v;
-      const int ts = min(src.base_t + t, src.last);
-      dma16(src.cp, (uint32_t)(ts * 1024) + lat_off[op & 3], src.tile + t * 1024);
-    } else {
+    if (op < (FP8 ? 4 : 8)) {
+      if constexpr (!FP8) {
+        const int t = 4 * op + v;
+        const int ts = min(src.base_t + t, src.last);
+        dma16(src.cp, (uint32_t)(ts * 1024) + lat_off[op & 3], src.tile + t * 1024);
+      } else {
+        const int q = 4 * op + v;                   // rows 2q (lanes 0-31), 2q+1 (32-63)
+        const int t = 2 * q + (lane >> 5);
+        const int ts = min(src.base_t + t, src.last);
+        const int jc = (lane & 31) ^ (t & 15);      // 16-B chunk of the 512-B row
+        dma16(src.cp, (uint32_t)(ts * 512 + jc * 16), src.tile + 2 * q * 512);
+      }
+    } else if (op == (FP8 ? 4 : 8)) {
       const int t = 8 * v + (lane >> 3);
       const int ts = min(src.base_t + t, src.last);
       const int jc = (lane & 7) ^ swz_rope(t);
       dma16(src.rp, (uint32_t)(ts * 128 + jc * 16), src.tile + kLatTile + v * 1024);
+    } else if constexpr (FP8) {
+      const int ts = min(src.base_t + (lane & 31), src.last);
+      dma4(src.sp, (uint32_t)(ts * 4), src.tile + Gm::kScaleOff);
     }
   };
   auto issue_tile = [&](int jt) __attribute__((always_inline)) {
     const TileSrc src = tile_src(jt);
 #pragma unroll
-    for (int op = 0; op < kDmaPerWave; ++op) dma_op(src, op);
+    for (int op = 0; op < 9; ++op)
+      if (op < n_ops) dma_op(src, op);
+  };
+  // this wave's copies of one tile must have landed: at most `pending` of the
+  // next tile's copies may still be in flight
+  auto wait_tile = [&](bool pending) __attribute__((always_inline)) {
+    if (!pending) wait_copies<0>();
+    else if (!FP8) wait_copies<9>();
+    else if (v == 0) wait_copies<6>();
+    else wait_copies<5>();
   };
 
   f32x4_t U[4][8];
@@ -367,23 +490,29 @@ void decode_mfma_bf16_kernel(DecodeParams p) {
   const int c0 = (i16 & 3) >> 1;
 
   issue_tile(0);
-  if (n_tiles > 1) {
-    issue_tile(1);
-    wait_copies<kDmaPerWave>();
-  } else {
-    wait_copies<0>();
-  }
+  if (n_tiles > 1) issue_tile(1);
+  wait_tile(n_tiles > 1);
 
   bf16x8_t pa[4];
   // half 0 issues copy ops 0..4 of the next-but-one tile between its MFMA
   // groups, half 1 ops 5..8 (when `more`)
   auto pv_half = [&](const lds_char* tile, int half, bool more, const TileSrc& src) __attribute__((always_inline)) {
-    const lds_char* const rowA = tile + (8 * G4 + (i16 >> 2)) * 1024 + 256 * v + (i16 & 1) * 8;
     auto bfrag = [&](int dt) __attribute__((always_inline)) -> bf16x8_t {
-      const int dx = (32 * dt) ^ xq32;              // 32 * (dt ^ xq)
-      const bf16x4_t lo = lds_read_tr16(rowA + dx + 16 * c0);                  // tokens +0..3
-      const bf16x4_t hi = lds_read_tr16(rowA + 4 * 1024 + dx + 16 * (c0 ^ 1)); // tokens +4..7
-      return concat(lo, hi);
+      if constexpr (!FP8) {
+        const lds_char* const rowA = tile + (8 * G4 + (i16 >> 2)) * 1024 + 256 * v + (i16 & 1) * 8;
+        const int dx = (32 * dt) ^ xq32;              // 32 * (dt ^ xq)
+        const bf16x4_t lo = lds_read_tr16(rowA + dx + 16 * c0);                  // tokens +0..3
+        const bf16x4_t hi = lds_read_tr16(rowA + 4 * 1024 + dx + 16 * (c0 ^ 1)); // tokens +4..7
+        return concat(lo, hi);
+      } else {
+        // lane 2r+h of each 16-lane group reads 8 bytes of token 8*G4 + r at
+        // latent byte 128*v + 16*dt + 8*h; the transposed read hands lane i
+        // the 8 tokens of column 128*v + 16*dt + i
+        const int r = i16 >> 1, h = i16 & 1;
+        const int ph8 = h + 2 * (dt ^ r) + 16 * (v ^ (G4 & 1));
+        const lds_char* const a = tile + (8 * G4 + r) * 512 + ph8 * 8;
+        return fp8x8_to_bf16(__builtin_amdgcn_ds_read_tr8_b64_v2i32((MLA_LDS i32x2_t*)a));
+      }
     };
     constexpr int kRingB = 2;
     bf16x8_t ringb[kRingB];
@@ -400,12 +529,19 @@ void decode_mfma_bf16_kernel(DecodeParams p) {
       if (e + kRingB < 4) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       if (more) {
-        if (half == 0) {
-          dma_op(src, e == 0 ? 0 : e + 1);
-          if (e == 0) dma_op(src, 1);
-        } else if (e < 3) {
-          dma_op(src, 5 + e);
-          if (e == 2) dma_op(src, 8);
+        if constexpr (!FP8) {
+          // 9 copies: 2 + 1 + 1 + 1 in the first half, 1 + 1 + 2 in the second
+          if (half == 0) {
+            dma_op(src, e == 0 ? 0 : e + 1);
+            if (e == 0) dma_op(src, 1);
+          } else if (e < 3) {
+            dma_op(src, 5 + e);
+            if (e == 2) dma_op(src, 8);
+          }
+        } else if (half == 0 && e < 3) {
+          // 5 or 6 copies, two per MFMA group
+          dma_op(src, 2 * e);
+          if (2 * e + 1 < n_ops) dma_op(src, 2 * e + 1);
         }
       }
     }
@@ -441,8 +577,7 @@ void decode_mfma_bf16_kernel(DecodeParams p) {
     lds_sync();  // (Y)
     if (j >= 1) pv_half(tile, 1, more, src);
     // tile j+1 must be resident at the next (X); tile j+2's copies may fly on
-    if (more) wait_copies<kDmaPerWave>();
-    else wait_copies<0>();
+    wait_tile(more);
   }
   lds_sync();  // (Z) row sums and reference maxima published
 
@@ -481,7 +616,12 @@ void decode_mfma_bf16_kernel(DecodeParams p) {
 }  // namespace
 
 hipError_t launch_decode_mfma_bf16(const DecodeParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(decode_mfma_bf16_kernel, dim3(p.per_xcd * kNumXcd), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL(decode_mfma_kernel<false>, dim3(p.per_xcd * kNumXcd), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_mfma_fp8(const DecodeParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(decode_mfma_kernel<true>, dim3(p.per_xcd * kNumXcd), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 

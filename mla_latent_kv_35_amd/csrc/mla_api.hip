@@ -192,7 +192,7 @@ int mla_decode_paged(const mla_decode_args* a, void* stream) {
   hipError_t e;
   if (a->ckv_dt == MLA_F32) e = launch_decode_simple_f32(p, s);
   else if (a->ckv_dt == MLA_BF16) e = launch_decode_mfma_bf16(p, s);
-  else return MLA_ERR_UNSUPPORTED;
+  else e = launch_decode_mfma_fp8(p, s);
   if (e != hipSuccess) return MLA_ERR_LAUNCH;
   if (pl.n_split > 1) {
     CombineParams c{};

@@ -13,6 +13,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
 
 #define MLA_LDS __attribute__((address_space(3)))
 typedef MLA_LDS char lds_char;

@@ -120,6 +120,14 @@ def test_small_fp32_parity(mla, split):
     check_against_oracle(mla, synth.make_inputs(cfg), split_tokens=split)
 
 
+@pytest.mark.parametrize("kw", SMALL)
+@pytest.mark.parametrize("split", [0, 64, 192])
+def test_small_fp8_parity(mla, kw, split):
+    # fp8 latent cache with per-token scales; the kernel also quantizes q_lat
+    cfg = synth.small_config(seed=300 + kw["B"] + kw["seq_len"], ckv_dt="fp8", **kw)
+    check_against_oracle(mla, synth.make_inputs(cfg), split_tokens=split)
+
+
 # --------------------------------------------------------------------------
 # the five workloads at full size
 # --------------------------------------------------------------------------
@@ -145,6 +153,15 @@ def test_long_128k_full(mla):
     check_against_oracle(mla, synth.make_inputs("long_128k"))
 
 
+def test_mtp_fp8_full_sampled(mla):
+    # B=128, T=2, S=8192, fp8 cache: every sequence runs on the GPU, a sample
+    # of them (first, last and six seeded picks) is checked row by row
+    inp = synth.make_inputs("mtp_fp8")
+    rng = np.random.default_rng(78)
+    pick = sorted(set([0, inp.cfg.B - 1] + rng.choice(inp.cfg.B, 6, replace=False).tolist()))
+    check_against_oracle(mla, inp, batches=pick)
+
+
 # --------------------------------------------------------------------------
 # bit-exact indexing and split/combine properties
 # --------------------------------------------------------------------------
@@ -164,23 +181,25 @@ def _ragged(seed=31, **kw):
     return synth.make_inputs(synth.small_config(seed=seed, **base))
 
 
-@pytest.mark.parametrize("split", [0, 64])
-def test_block_table_permutation_bit_exact(mla, split):
-    a = _ragged()
-    b = _ragged()
+@pytest.mark.parametrize("split,ckv_dt", [(0, "bf16"), (64, "bf16"), (0, "fp8"), (64, "fp8")])
+def test_block_table_permutation_bit_exact(mla, split, ckv_dt):
+    a = _ragged(ckv_dt=ckv_dt)
+    b = _ragged(ckv_dt=ckv_dt)
     perm = np.random.default_rng(1).permutation(b.n_pages)
     inv = np.argsort(perm)
     b.ckv, b.kr = b.ckv[inv], b.kr[inv]
+    if b.ckv_scale is not None:
+        b.ckv_scale = b.ckv_scale[inv]
     b.block_table = np.where(b.block_table >= 0, perm[np.maximum(b.block_table, 0)], -1).astype(np.int32)
     ua, la = _decode_u(mla, a, split)
     ub, lb = _decode_u(mla, b, split)
     assert np.array_equal(ua, ub) and np.array_equal(la, lb)
 
 
-@pytest.mark.parametrize("T", [1, 2])
-def test_poisoned_tails_bit_exact(mla, T):
-    a = _ragged(T=T)
-    b = _ragged(T=T)
+@pytest.mark.parametrize("T,ckv_dt", [(1, "bf16"), (2, "bf16"), (1, "fp8"), (2, "fp8")])
+def test_poisoned_tails_bit_exact(mla, T, ckv_dt):
+    a = _ragged(T=T, ckv_dt=ckv_dt)
+    b = _ragged(T=T, ckv_dt=ckv_dt)
     synth.poison_unused_slots(b)
     ua, la = _decode_u(mla, a)
     ub, lb = _decode_u(mla, b)
