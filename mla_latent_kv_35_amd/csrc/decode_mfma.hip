@@ -48,8 +48,8 @@ constexpr int kThreads = 512;
 constexpr int kTileTok = 32;
 constexpr int kRopeTile = kTileTok * 128;           // 4096: rope rows of 128 B (bf16)
 constexpr int kNumBuf = 4;
-constexpr int kPStride = 80;                        // bytes per probability row (32 bf16 + pad)
-constexpr int kPBytes = kRowsPerGroup * kPStride;   // 5120
+constexpr int kPStride = 64;                        // bytes per probability row (32 bf16)
+constexpr int kPBytes = kRowsPerGroup * kPStride;   // 4096
 
 // LDS tile geometry: latent rows of 1 KB (bf16) or 512 B (fp8), then the rope
 // rows, then (fp8) the tile's 32 token scales in a 256-B slot.
@@ -79,13 +79,30 @@ struct Geo {
 // u, l and lse do not depend on the reference.
 constexpr float kLazyMax = 8.0f;
 
-// Latent rows: 16-B chunk j of token t lives at chunk j ^ swz_lat(t & 15).
-// swz_lat is a bijection of 0..15, so 16 consecutive tokens reading the same
-// chunk hit 16 different chunk columns (all 64 banks), and for the transposed
-// reads (4 consecutive tokens x 2 adjacent chunks per 16-lane group, groups
-// 8 tokens apart) the 32 lanes of a pass cover 64 distinct banks.
+// LDS bank rules of gfx950 that the layouts below are built for (measured
+// with the SQ_LDS_BANK_CONFLICT counter): ds_read_b64 and ds_read_b64_tr_*
+// serve lanes 0-31 and 32-63 in one pass each over 64 banks (256 B);
+// ds_read_b128 serves four passes of 16 lanes, lanes 0-31 and 32-63 apart and,
+// within each half, the 4-lane quads q = lane/4 split by the parity of q's
+// bits; ds_write_b64 / _b128 serve 16 / 8 consecutive lanes per pass over 32
+// banks (128 B).
+//
+// Latent rows: 16-B chunk j of token t lives at chunk j ^ swz_lat(t & 15),
+// swz_lat(s) = s3 s1 s0 0 (binary). The score team's ds_read_b128 (16 tokens
+// x one chunk per k-step, tokens t and t^4 in different passes) and the
+// transposed reads (4 consecutive tokens x 2 adjacent chunks per 16-lane
+// group, groups 8 tokens apart, 32 lanes per pass) then touch 64 distinct
+// banks per pass.
 __device__ __forceinline__ int swz_lat(int s) {
-  return (s & 8) | ((s & 3) << 1) | ((s >> 2) & 1);
+  return (s & 8) | ((s & 3) << 1);
+}
+// Probability rows (64 B = 8 units of 8 B): unit u of row r lives at
+// u ^ swz_p(r & 15), swz_p(r) = r3 r1 r2 (binary). The score team writes one
+// unit per lane (16 rows per pass: 8 distinct units per row parity) and the
+// aggregation team reads units 2g and 2g+1 (32 lanes per pass: rows r, r+4,
+// r+8, r+12 fall in distinct unit pairs).
+__device__ __forceinline__ int swz_p(int r) {
+  return ((r >> 2) & 1) | (r & 2) | (((r >> 3) & 1) << 2);
 }
 // Rope rows (128 B): chunk j (0..7) of token t lives at chunk j ^ ((t>>1)&7).
 __device__ __forceinline__ int swz_rope(int t) { return (t >> 1) & 7; }
@@ -383,7 +400,7 @@ void decode_mfma_kernel(DecodeParams p) {
             hi = pack_bf16x2(e2 * tsc[2], e3 * tsc[3]);
             ls = (e0 + e1) + (e2 + e3);
           }
-          *(MLA_LDS u32x2_t*)(pj + rr * kPStride + (16 * th + 4 * G4) * 2) = (u32x2_t){lo, hi};
+          *(MLA_LDS u32x2_t*)(pj + rr * kPStride + 8 * ((4 * th + G4) ^ swz_p(i16))) = (u32x2_t){lo, hi};
           l_s[ht] = l_s[ht] * alpha + wave_sum16(ls);
         }
       }
@@ -502,7 +519,7 @@ void decode_mfma_kernel(DecodeParams p) {
         const lds_char* const rowA = tile + (8 * G4 + (i16 >> 2)) * 1024 + 256 * v + (i16 & 1) * 8;
         const int dx = (32 * dt) ^ xq32;              // 32 * (dt ^ xq)
         const bf16x4_t lo = lds_read_tr16(rowA + dx + 16 * c0);                  // tokens +0..3
-        const bf16x4_t hi = lds_read_tr16(rowA + 4 * 1024 + dx + 16 * (c0 ^ 1)); // tokens +4..7
+        const bf16x4_t hi = lds_read_tr16(rowA + 4 * 1024 + dx + 16 * c0);     // tokens +4..7
         return concat(lo, hi);
       } else {
         // lane 2r+h of each 16-lane group reads 8 bytes of token 8*G4 + r at
@@ -565,7 +582,14 @@ void decode_mfma_kernel(DecodeParams p) {
       }
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt)
-        pa[rt] = lds_read_b128(pj + (16 * rt + i16) * kPStride + 16 * G4);
+      {
+        // P row 16*rt + i16, tokens 8*G4 .. 8*G4+7 (units 2*G4, 2*G4+1)
+        const lds_char* const prow = pj + (16 * rt + i16) * kPStride;
+        const int sp = swz_p(i16);
+        const bf16x4_t p0 = *(const MLA_LDS bf16x4_t*)(prow + 8 * ((2 * G4) ^ sp));
+        const bf16x4_t p1 = *(const MLA_LDS bf16x4_t*)(prow + 8 * ((2 * G4 + 1) ^ sp));
+        pa[rt] = concat(p0, p1);
+      }
       if (__builtin_amdgcn_ballot_w64(rescale)) {
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
