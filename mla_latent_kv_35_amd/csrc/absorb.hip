@@ -2,8 +2,8 @@
 // analysis", section 1.2 and section 6): q_lat[n][h][:] = W_UK[h]^T q[n][h][:],
 // so the score q^T (W^UK c) becomes q_lat . c against the cached latent.
 //
-// bf16: one workgroup per (head h, 128-wide latent block, 256-token block).
-// The weight block W_UK[h][0:128][d0:d0+128] is staged in LDS with the same
+// bf16: one workgroup per (head h, 128-wide latent block, 32 tokens), the
+// blocks of one head on one XCD. The weight block W_UK[h][0:128][d0:d0+128] is staged in LDS with the same
 // 16-byte XOR swizzle the decode kernel uses and read transposed
 // (ds_read_b64_tr_b16) as the K-major MFMA operand; the queries are read
 // straight from global memory as the other operand. fp32: plain fp32 FMA.
@@ -14,7 +14,7 @@ namespace mla {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTokBlock = 256;
+constexpr int kTokTile = 32;
 
 __device__ __forceinline__ int swz16(int s) { return (s & 8) | ((s & 3) << 1) | ((s >> 2) & 1); }
 
@@ -22,23 +22,46 @@ template <bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) void absorb_bf16_kernel(const uint16_t* __restrict__ q,
                                                                const uint16_t* __restrict__ wuk,
                                                                void* __restrict__ out, int n_tok,
-                                                               int H) {
+                                                               int H, int n_tb) {
   __shared__ __attribute__((aligned(16))) char smem_raw[kDh * 256];
   lds_char* smem = (lds_char*)smem_raw;
-  const int h = blockIdx.x;
-  const int d0 = blockIdx.y * 128;
-  const int n_base = blockIdx.z * kTokBlock;
+  // blocks on XCD x (= blockIdx % 8) serve the heads h with h % 8 == x
+  const int x = blockIdx.x % kNumXcd, idx = blockIdx.x / kNumXcd;
+  const int per_head = 4 * n_tb;
+  const int h = kNumXcd * (idx / per_head) + x;
+  if (h >= H) return;
+  const int tb = (idx % per_head) >> 2;
+  const int d0 = 128 * (idx & 3);
+  const int n0 = tb * kTokTile;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int i16 = lane & 15, G4 = lane >> 4;
 
-  // stage W_UK[h][j][d0 .. d0+127]: row j = 16 chunks of 16 B, chunk c at c ^ swz16(j & 15)
+  // queries of the block's 32 tokens (A operand rows) and the weight block
+  // W_UK[h][0:128][d0:d0+128] are both in flight before anything waits
+  bf16x8_t a[2][4];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const int na = n0 + 16 * tt + i16;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if (na < n_tok) a[tt][ks] = load_bf16x8(q + ((size_t)na * H + h) * kDh + 32 * ks + 8 * G4);
+      else a[tt][ks] = (bf16x8_t){0, 0, 0, 0, 0, 0, 0, 0};
+    }
+  }
   const uint16_t* wh = wuk + (size_t)h * kDh * kDc + d0;
+  u32x4_t wv[(kDh * 16) / kThreads];
 #pragma unroll
   for (int e = 0; e < (kDh * 16) / kThreads; ++e) {
-    const int idx = e * kThreads + tid;
-    const int j = idx >> 4, c = idx & 15;
-    const u32x4_t v = *(const u32x4_t*)(wh + (size_t)j * kDc + 8 * c);
-    *(MLA_LDS u32x4_t*)(smem + j * 256 + ((c ^ swz16(j & 15)) * 16)) = v;
+    const int idx2 = e * kThreads + tid;
+    const int j = idx2 >> 4, c = idx2 & 15;
+    wv[e] = *(const u32x4_t*)(wh + (size_t)j * kDc + 8 * c);
+  }
+  // stage the weight block: row j = 16 chunks of 16 B, chunk c at c ^ swz16(j & 15)
+#pragma unroll
+  for (int e = 0; e < (kDh * 16) / kThreads; ++e) {
+    const int idx2 = e * kThreads + tid;
+    const int j = idx2 >> 4, c = idx2 & 15;
+    *(MLA_LDS u32x4_t*)(smem + j * 256 + ((c ^ swz16(j & 15)) * 16)) = wv[e];
   }
   __syncthreads();
 
@@ -57,25 +80,17 @@ __global__ __launch_bounds__(kThreads) void absorb_bf16_kernel(const uint16_t* _
       bw[u][ks] = concat(lo, hi);
     }
   }
-
-  const int n_end = min(n_tok, n_base + kTokBlock);
-  for (int n0 = n_base; n0 < n_end; n0 += 16) {
-    const int na = n0 + i16;
-    bf16x8_t a[4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      if (na < n_tok) a[ks] = load_bf16x8(q + ((size_t)na * H + h) * kDh + 32 * ks + 8 * G4);
-      else a[ks] = (bf16x8_t){0, 0, 0, 0, 0, 0, 0, 0};
-    }
+  for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) acc = mfma16x16x32(a[ks], bw[u][ks], acc);
+      for (int ks = 0; ks < 4; ++ks) acc = mfma16x16x32(a[tt][ks], bw[u][ks], acc);
       const int d = d0 + 16 * (2 * w + u) + i16;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int n = n0 + 4 * G4 + i;
+        const int n = n0 + 16 * tt + 4 * G4 + i;
         if (n < n_tok) {
           const size_t o = ((size_t)n * H + h) * kDc + d;
           if (OUT_BF16) ((uint16_t*)out)[o] = f2bf(acc[i]);
@@ -83,7 +98,6 @@ __global__ __launch_bounds__(kThreads) void absorb_bf16_kernel(const uint16_t* _
         }
       }
     }
-  }
 }
 
 __global__ __launch_bounds__(kThreads) void absorb_f32_kernel(const float* __restrict__ q,
@@ -109,13 +123,14 @@ hipError_t launch_absorb(const void* q_nope, const void* w_uk, void* q_lat, int 
                          int out_bf16, int n_tok, int H, hipStream_t s) {
   if (n_tok == 0) return hipSuccess;
   if (in_bf16) {
-    dim3 grid(H, kDc / 128, (n_tok + kTokBlock - 1) / kTokBlock);
+    const int n_tb = (n_tok + kTokTile - 1) / kTokTile;
+    const dim3 grid(kNumXcd * ((H + kNumXcd - 1) / kNumXcd) * 4 * n_tb);
     if (out_bf16)
       hipLaunchKernelGGL(absorb_bf16_kernel<true>, grid, dim3(kThreads), 0, s,
-                         (const uint16_t*)q_nope, (const uint16_t*)w_uk, q_lat, n_tok, H);
+                         (const uint16_t*)q_nope, (const uint16_t*)w_uk, q_lat, n_tok, H, n_tb);
     else
       hipLaunchKernelGGL(absorb_bf16_kernel<false>, grid, dim3(kThreads), 0, s,
-                         (const uint16_t*)q_nope, (const uint16_t*)w_uk, q_lat, n_tok, H);
+                         (const uint16_t*)q_nope, (const uint16_t*)w_uk, q_lat, n_tok, H, n_tb);
   } else {
     hipLaunchKernelGGL(absorb_f32_kernel, dim3(n_tok * H), dim3(kThreads), 0, s,
                        (const float*)q_nope, (const float*)w_uk, (float*)q_lat, n_tok, H);

@@ -14,6 +14,7 @@ typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef int i32x2_t __attribute__((ext_vector_type(2)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
 #define MLA_LDS __attribute__((address_space(3)))
 typedef MLA_LDS char lds_char;
@@ -27,8 +28,13 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
   return __builtin_bit_cast(uint16_t, b);
 }
 
+// two binary32 -> packed bfloat16 pair (one v_cvt_pk_bf16_f32, round to
+// nearest even); lo in bits 15:0.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+  typedef float f2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
+  const b2_t v = __builtin_convertvector((f2_t){lo, hi}, b2_t);
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // D = A(16x32) * B(32x16) + C on bf16 inputs with fp32 accumulation.

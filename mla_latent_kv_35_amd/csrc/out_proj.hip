@@ -2,10 +2,9 @@
 // DeepSeek-V2 analysis", section 6.1: each head aggregates latents with its
 // own weights first, then applies its own matrix): o[n][h][:] = W_UV[h] u[n][h][:].
 //
-// bf16: one workgroup per (head h, 64 output dims, 256-token block); each wave
-// owns 16 output dims. Both MFMA operands are contiguous along the reduced
-// latent axis in memory (u rows and W_UV rows), so they load straight from
-// global memory. fp32: plain fp32 FMA.
+// bf16 weights: MFMA with both operands contiguous along the reduced latent
+// axis in memory (u rows and W_UV rows), so they load straight from global
+// memory. fp32: plain fp32 FMA.
 #include "mla_device.h"
 #include "mla_internal.h"
 
@@ -13,7 +12,6 @@ namespace mla {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTokBlock = 256;
 
 __device__ __forceinline__ bf16x8_t load_row8(const void* base, size_t off, bool bf16) {
   if (bf16) return load_bf16x8((const uint16_t*)base + off);
@@ -28,42 +26,59 @@ __device__ __forceinline__ bf16x8_t load_row8(const void* base, size_t off, bool
   return r;
 }
 
+// One workgroup per (head h, 64 output dims, 32 tokens); wave w owns output
+// dims 64*jb + 16*w .. +15 for the 32 tokens (two 16-token MFMA tiles). All
+// of a wave's operand loads (its 16 W_UV rows and the 32 u rows) are issued
+// before its first MFMA. Workgroups are placed so that the blocks of one
+// head, which read the same u rows, share an XCD (and its L2).
+constexpr int kTokTile = 32;
+
 template <bool U_BF16, bool O_BF16>
 __global__ __launch_bounds__(kThreads) void out_proj_bf16_kernel(const void* __restrict__ u,
                                                                  const uint16_t* __restrict__ wuv,
                                                                  void* __restrict__ o, int n_tok,
-                                                                 int H) {
-  const int h = blockIdx.x;
+                                                                 int H, int n_tb) {
+  // blocks on XCD x (= blockIdx % 8) serve the heads h with h % 8 == x
+  const int x = blockIdx.x % kNumXcd, idx = blockIdx.x / kNumXcd;
+  const int per_head = 2 * n_tb;
+  const int h = kNumXcd * (idx / per_head) + x;
+  if (h >= H) return;
+  const int tb = (idx % per_head) >> 1, jb = idx & 1;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int i16 = lane & 15, G4 = lane >> 4;
-  const int j = 64 * blockIdx.y + 16 * w + i16;       // this lane's output dim (B column)
-  const int n_base = blockIdx.z * kTokBlock;
+  const int j = 64 * jb + 16 * w + i16;               // this lane's output dim (B column)
+  const int n0 = tb * kTokTile;
 
   bf16x8_t bw[16];
   const uint16_t* wrow = wuv + ((size_t)h * kDh + j) * kDc + 8 * G4;
 #pragma unroll
   for (int ks = 0; ks < 16; ++ks) bw[ks] = load_bf16x8(wrow + 32 * ks);
-
-  const int n_end = min(n_tok, n_base + kTokBlock);
-  for (int n0 = n_base; n0 < n_end; n0 += 16) {
-    const int na = n0 + i16;
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  bf16x8_t a[2][16];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const int na = n0 + 16 * tt + i16;                // this lane's token (A row)
 #pragma unroll
     for (int ks = 0; ks < 16; ++ks) {
-      bf16x8_t a = (bf16x8_t){0, 0, 0, 0, 0, 0, 0, 0};
-      if (na < n_tok) a = load_row8(u, ((size_t)na * H + h) * kDc + 32 * ks + 8 * G4, U_BF16);
-      acc = mfma16x16x32(a, bw[ks], acc);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int n = n0 + 4 * G4 + i;
-      if (n < n_tok) {
-        const size_t off = ((size_t)n * H + h) * kDh + j;
-        if (O_BF16) ((uint16_t*)o)[off] = f2bf(acc[i]);
-        else ((float*)o)[off] = acc[i];
-      }
+      a[tt][ks] = (bf16x8_t){0, 0, 0, 0, 0, 0, 0, 0};
+      if (na < n_tok) a[tt][ks] = load_row8(u, ((size_t)na * H + h) * kDc + 32 * ks + 8 * G4, U_BF16);
     }
   }
+  f32x4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int ks = 0; ks < 16; ++ks)
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) acc[tt] = mfma16x16x32(a[tt][ks], bw[ks], acc[tt]);
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int n = n0 + 16 * tt + 4 * G4 + i;
+      if (n < n_tok) {
+        const size_t off = ((size_t)n * H + h) * kDh + j;
+        if (O_BF16) ((uint16_t*)o)[off] = f2bf(acc[tt][i]);
+        else ((float*)o)[off] = acc[tt][i];
+      }
+    }
 }
 
 __global__ __launch_bounds__(kDh) void out_proj_f32_kernel(const float* __restrict__ u,
@@ -87,16 +102,17 @@ hipError_t launch_out_proj(const void* u, const void* w_uv, void* o, int u_bf16,
                            int o_bf16, int n_tok, int H, hipStream_t s) {
   if (n_tok == 0) return hipSuccess;
   if (w_bf16) {
-    dim3 grid(H, kDh / 64, (n_tok + kTokBlock - 1) / kTokBlock);
+    const int n_tb = (n_tok + kTokTile - 1) / kTokTile;
+    const dim3 grid(kNumXcd * ((H + kNumXcd - 1) / kNumXcd) * 2 * n_tb);
     const uint16_t* w = (const uint16_t*)w_uv;
     if (u_bf16 && o_bf16)
-      hipLaunchKernelGGL((out_proj_bf16_kernel<true, true>), grid, dim3(kThreads), 0, s, u, w, o, n_tok, H);
+      hipLaunchKernelGGL((out_proj_bf16_kernel<true, true>), grid, dim3(kThreads), 0, s, u, w, o, n_tok, H, n_tb);
     else if (u_bf16)
-      hipLaunchKernelGGL((out_proj_bf16_kernel<true, false>), grid, dim3(kThreads), 0, s, u, w, o, n_tok, H);
+      hipLaunchKernelGGL((out_proj_bf16_kernel<true, false>), grid, dim3(kThreads), 0, s, u, w, o, n_tok, H, n_tb);
     else if (o_bf16)
-      hipLaunchKernelGGL((out_proj_bf16_kernel<false, true>), grid, dim3(kThreads), 0, s, u, w, o, n_tok, H);
+      hipLaunchKernelGGL((out_proj_bf16_kernel<false, true>), grid, dim3(kThreads), 0, s, u, w, o, n_tok, H, n_tb);
     else
-      hipLaunchKernelGGL((out_proj_bf16_kernel<false, false>), grid, dim3(kThreads), 0, s, u, w, o, n_tok, H);
+      hipLaunchKernelGGL((out_proj_bf16_kernel<false, false>), grid, dim3(kThreads), 0, s, u, w, o, n_tok, H, n_tb);
   } else {
     hipLaunchKernelGGL(out_proj_f32_kernel, dim3(n_tok * H), dim3(kDh), 0, s, (const float*)u,
                        (const float*)w_uv, (float*)o, H);

@@ -65,10 +65,12 @@ def check_against_oracle(mla, inp, batches=None, split_tokens=0, tol=None):
 # --------------------------------------------------------------------------
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
-def test_rope_parity_long_positions(mla, dt):
+@pytest.mark.parametrize("H,dr", [(8, 64), (40, 64), (128, 64), (8, 32)])
+def test_rope_parity_long_positions(mla, dt, H, dr):
+    # H=40: a partial block of heads; dr=32: the general (non-64) kernel
     rng = np.random.default_rng(0)
     pos = np.array([0, 1, 63, 4095, 4096, 32767, 131071], dtype=np.int32)
-    x = synth.store(rng.standard_normal((len(pos), 8, 64)), dt)
+    x = synth.store(rng.standard_normal((len(pos), H, dr)), dt)
     xd = mla.to_device(x, dt)
     y = host(mla.rope(xd, mla.to_device(pos, "i32")))
     ref = O.rope_rotate(O.stored_to_f64(x, dt), pos)
