@@ -64,7 +64,13 @@ struct Geo {
   static constexpr int kOffRed = kOffAlpha + 2 * 64 * 4;    // tile maxima [2][64] f32
   static constexpr int kOffLsum = kOffRed + 2 * 64 * 4;     // row sums [2][64] f32
   static constexpr int kOffM = kOffLsum + 2 * 64 * 4;       // final reference max [64] f32
-  static constexpr int kOffIds = kOffM + 64 * 4;            // page ids of the split
+  // before step 0 the absorbed queries pass through LDS once per workgroup
+  // (72 KB from tile buffer 2 on; bf16: buffers 2-3, fp8: also the P and
+  // per-row arrays, all first written after the first step's barrier)
+  static constexpr int kOffStage = 2 * kTileBytes;
+  static constexpr int kStageBytes = 2 * 2 * 18 * 1024;
+  static constexpr int kOffIds = (kOffM + 64 * 4 > kOffStage + kStageBytes) ? kOffM + 64 * 4
+                                                                            : kOffStage + kStageBytes;
   static constexpr int kLdsBytes = kOffIds + kMaxSplitPages * 4;
   // page copies per tile per aggregation wave: bf16 8 latent rows + 1 rope
   // block; fp8 4 latent row pairs + 1 rope block (+ the scales on wave 0)
@@ -248,31 +254,53 @@ void decode_mfma_kernel(DecodeParams p) {
     // ======================= score team ======================================
     const int hh = w & 1;    // rows 32*hh..+31
     const int th = w >> 1;   // tokens 16*th..+15 of each tile
-    // absorbed queries of this wave's rows, loaded while the aggregation team
-    // checks the block table
-    // query fragments: 16 latent k-steps + 2 rope k-steps per 16-row half
+    // Absorbed queries of the wave's 32 rows as MFMA B fragments: 16 latent
+    // k-steps + 2 rope k-steps per 16-row half. The two waves of a row half
+    // (th = 0, 1) each load 9 of the 18 k-steps from global memory (issued
+    // before the block-table check, which they do not depend on), stage them
+    // in LDS and take the partner's 9 from there, so the workgroup reads its
+    // queries from memory once.
     bf16x8_t qB[2][18];
-    const bool active = !seq_bad && tok0 < tok1;
+    lds_char* const stage = smem + Gm::kOffStage;
+    auto stage_at = [&](int ht, int ks) __attribute__((always_inline)) -> lds_char* {
+      return stage + (((hh * 2 + ht) * 18 + ks) * 64 + lane) * 16;
+    };
+    auto q_half = [&](auto half_c, bool from_lds) __attribute__((always_inline)) {
+      constexpr int k0 = 9 * decltype(half_c)::value;
 #pragma unroll
-    for (int ht = 0; ht < 2; ++ht) {
-      const int r = row0 + 32 * hh + 16 * ht + i16;
-      if (active && r < p.R) {
+      for (int ht = 0; ht < 2; ++ht) {
+        const int r = row0 + 32 * hh + 16 * ht + i16;
         const uint16_t* ql = (const uint16_t*)p.q_lat + ((size_t)b * p.R + r) * kDc + 8 * G4;
         const uint16_t* qr = (const uint16_t*)p.q_rope + ((size_t)b * p.R + r) * kDr + 8 * G4;
 #pragma unroll
-        for (int ks = 0; ks < 16; ++ks) qB[ht][ks] = load_bf16x8(ql + 32 * ks);
-        qB[ht][16] = load_bf16x8(qr);
-        qB[ht][17] = load_bf16x8(qr + 32);
-      } else {
-#pragma unroll
-        for (int ks = 0; ks < 18; ++ks) qB[ht][ks] = (bf16x8_t){0, 0, 0, 0, 0, 0, 0, 0};
+        for (int kk = 0; kk < 9; ++kk) {
+          const int ks = k0 + kk;
+          if (from_lds) qB[ht][ks] = lds_read_b128(stage_at(ht, ks));
+          else if (r >= p.R) qB[ht][ks] = (bf16x8_t){0, 0, 0, 0, 0, 0, 0, 0};
+          else qB[ht][ks] = load_bf16x8(ks < 16 ? ql + 32 * ks : qr + 32 * (ks - 16));
+        }
       }
-    }
+    };
+    auto q_stage = [&](auto half_c) __attribute__((always_inline)) {
+      constexpr int k0 = 9 * decltype(half_c)::value;
+#pragma unroll
+      for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+        for (int kk = 0; kk < 9; ++kk)
+          *(MLA_LDS bf16x8_t*)stage_at(ht, k0 + kk) = qB[ht][k0 + kk];
+    };
+    if (th == 0) q_half(std::integral_constant<int, 0>{}, false);
+    else q_half(std::integral_constant<int, 1>{}, false);
     if (seq_bad || __syncthreads_or(false)) {
       write_uniform_result(p, b, k, g, __builtin_nanf(""));
       return;
     }
     if (tok0 >= tok1) return;   // split past the end of the sequence: no partial
+    if (th == 0) q_stage(std::integral_constant<int, 0>{});
+    else q_stage(std::integral_constant<int, 1>{});
+    lds_sync();  // (Q) both halves staged
+    if (th == 0) q_half(std::integral_constant<int, 1>{}, true);
+    else q_half(std::integral_constant<int, 0>{}, true);
     // visible-token limit of a row: s < min(L - T + t + 1, tok1)
     auto row_limit = [&](int rr) __attribute__((always_inline)) -> int {
       const int r = row0 + rr;
@@ -288,7 +316,11 @@ void decode_mfma_kernel(DecodeParams p) {
     float m_s[2] = {-INFINITY, -INFINITY};
     float l_s[2] = {0.f, 0.f};
 
-    for (int j = 0; j <= n_tiles; ++j) {
+    // one step: scores of tile j, then the softmax of tile j; compiled with
+    // and without the causal / ragged-end mask, which only the tiles that
+    // reach past the group's first row limit need
+    auto step = [&](int j, auto masked_c) __attribute__((always_inline)) {
+      constexpr bool kMasked = decltype(masked_c)::value;
       lds_sync();  // (X) tile j resident
       f32x4_t S[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
       const int stok0 = tok0 + j * kTileTok;   // first token of tile j
@@ -355,21 +387,21 @@ void decode_mfma_kernel(DecodeParams p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) S[ht][i] = fmaf(Sl[ht][i], tsc[i], S[ht][i]);
         }
-        // scale, mask, tile maxima of this wave's rows
-        const bool masked = stok0 + kTileTok > lim_min;
+        // mask, tile maxima of this wave's rows; the scores stay unscaled
+        // and the scale (> 0, so it commutes with max) is applied to the
+        // maxima here and inside the exponent below
         float mx[2] = {-INFINITY, -INFINITY};
 #pragma unroll
         for (int ht = 0; ht < 2; ++ht)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            float z = S[ht][i] * p.scale_log2;
-            if (masked && stok0 + 16 * th + 4 * G4 + i >= lim_s[ht]) z = -INFINITY;
-            S[ht][i] = z;
-            mx[ht] = fmaxf(mx[ht], z);
+            if constexpr (kMasked)
+              if (stok0 + 16 * th + 4 * G4 + i >= lim_s[ht]) S[ht][i] = -INFINITY;
+            mx[ht] = fmaxf(mx[ht], S[ht][i]);
           }
 #pragma unroll
         for (int ht = 0; ht < 2; ++ht) {
-          mx[ht] = wave_max16(mx[ht]);
+          mx[ht] = wave_max16(mx[ht]) * p.scale_log2;
           if (lane < 16) redmax[th * 64 + 32 * hh + 16 * ht + lane] = mx[ht];
         }
       }
@@ -387,8 +419,9 @@ void decode_mfma_kernel(DecodeParams p) {
           const float alpha = (mnew == mold) ? 1.f : fast_exp2(mold - mnew);
           m_s[ht] = mnew;
           if (th == 0 && lane < 16) aj[rr] = alpha;
-          const float e0 = fast_exp2(S[ht][0] - base), e1 = fast_exp2(S[ht][1] - base);
-          const float e2 = fast_exp2(S[ht][2] - base), e3 = fast_exp2(S[ht][3] - base);
+          const float nb = -base, sc = p.scale_log2;
+          const float e0 = fast_exp2(fmaf(S[ht][0], sc, nb)), e1 = fast_exp2(fmaf(S[ht][1], sc, nb));
+          const float e2 = fast_exp2(fmaf(S[ht][2], sc, nb)), e3 = fast_exp2(fmaf(S[ht][3], sc, nb));
           uint32_t lo, hi;
           float ls;
           if constexpr (!FP8) {
@@ -404,6 +437,10 @@ void decode_mfma_kernel(DecodeParams p) {
           l_s[ht] = l_s[ht] * alpha + wave_sum16(ls);
         }
       }
+    };
+    for (int j = 0; j <= n_tiles; ++j) {
+      if (tok0 + j * kTileTok + kTileTok > lim_min) step(j, std::true_type{});
+      else step(j, std::false_type{});
     }
     if (lane < 16) {
       lsum[th * 64 + 32 * hh + lane] = l_s[0];
@@ -508,6 +545,7 @@ void decode_mfma_kernel(DecodeParams p) {
 
   issue_tile(0);
   if (n_tiles > 1) issue_tile(1);
+  lds_sync();  // (Q) the score team's queries staged; the copies fly on
   wait_tile(n_tiles > 1);
 
   bf16x8_t pa[4];
