@@ -25,7 +25,10 @@
 // Per step: barrier X (tile j resident, P(j-1) published), barrier Y (score
 // team's tile maxima published). Four tile buffers keep two tiles in flight
 // while two are in use. All barriers order LDS only; the page copies are
-// waited for explicitly with vmcnt by the waves that issued them.
+// waited for explicitly with vmcnt by the waves that issued them. Before
+// step 0 the absorbed queries pass through LDS once: each score wave loads
+// half of its rows' fragments and takes the other half from its partner
+// wave, while the first two tiles are already being copied.
 //
 // fp8 latent caches: tiles stay fp8 in LDS (half the bytes of bf16); every
 // E4M3FN code is widened exactly to bf16 in registers right before its MFMA,
