@@ -196,6 +196,28 @@ def main():
     torch.cuda.synchronize()
     dur_ms = {"decode": e0.elapsed_time(e1) / (n_dec * per_graph)}
 
+    # cache append of one step's new tokens (B*T), outside the step: into a
+    # pool of the same shape, at the tokens' own positions
+    c0 = caches[0]
+    app_cache = mla.PagedCache(torch.empty_like(c0.ckv), torch.empty_like(c0.kr),
+                               None if c0.ckv_scale is None else torch.empty_like(c0.ckv_scale),
+                               c0.block_table, c0.seq_lens, c0.max_seq_len, c0.total_tokens)
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    c_new = torch.randn((BT, 512), device="cuda", generator=gen).to(torch.bfloat16)
+    k_new = torch.randn((BT, 64), device="cuda", generator=gen).to(torch.bfloat16)
+    seq_new = torch.arange(cfg.B, device="cuda", dtype=torch.int32).repeat_interleave(cfg.T)
+    g_app = capture(lambda i: mla.cache_append(app_cache, c_new, k_new, seq_new, d.positions,
+                                               normalize=True), per_graph)
+    g_app.replay()
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a0.record(stream)
+    for _ in range(n_dec):
+        g_app.replay()
+    a1.record(stream)
+    torch.cuda.synchronize()
+    dur_ms["append"] = a0.elapsed_time(a1) / (n_dec * per_graph)
+
     tokens = cfg.B * cfg.T
     value = tokens * steps / el
     dec_s = dur_ms["decode"] * 1e-3
@@ -222,6 +244,7 @@ def main():
         "hbm_pct_of_peak": round(100 * achieved / PEAK_HBM_GBPS, 2),
         "decode_ms": round(dur_ms["decode"], 5),
         "eager_ms_per_step": round(el_eager / steps * 1e3, 5),
+        "append_ms": round(dur_ms["append"], 5),
         "launch": "hip graph of %d steps per replay" % per_graph,
         "roofline": {
             "kernel": "mla_decode_paged (split-KV kernel + log-sum-exp combine)",

@@ -174,6 +174,61 @@ int mla_decode_paged(const mla_decode_args* args, void* stream);
 int mla_out_proj(const void* u, const void* w_uv, void* o, int u_dt, int w_dt,
                  int o_dt, int n_tok, int H, int d_h, int d_c, void* stream);
 
+/*
+ * Arguments of the cache append: the step that puts each new token's cache
+ * entry into the paged pools before attention. Each token contributes its
+ * joint KV latent c (d_c = 512) and its shared rope key k^R (d_R = 64): the
+ * 576 elements that join the cache (V2 analysis page, section 1.3, and the
+ * walk through one token's path in section 6.3). The latent passes through
+ * an RMSNorm after the down-projection (same page, section 1.2: the report
+ * puts an RMSNorm after the compressed latents; its gain is not given, so it
+ * is an argument here). The rope key is rotated at the token's own position
+ * and cached already rotated (section 6, third absorption condition).
+ */
+typedef struct mla_append_args {
+  int32_t n_tok;              /* new tokens (>= 0; 0 launches nothing) */
+  int32_t B;                  /* sequences = rows of block_table (>= 1) */
+  int32_t d_c, d_r;           /* must be 512 and 64 */
+  int32_t page_size;          /* must be 64 */
+  int32_t n_pages;            /* pages in each pool (>= 1) */
+  int32_t max_pages_per_seq;  /* columns of block_table (>= 1) */
+  int32_t c_dt, k_dt;         /* input dtypes: F32 or BF16 */
+  int32_t ckv_dt, kr_dt;      /* pool dtypes: ckv F32, BF16 or FP8_E4M3; kr F32 or BF16 */
+  int32_t normalize;          /* 1: RMSNorm the latent before storing it; 0: store it as given */
+  float rms_eps;              /* RMSNorm epsilon (>= 0, finite) */
+  int32_t reserved0;          /* must be 0 */
+  double rope_base;           /* > 0; angles pos * base^(-2i/64), as mla_rope */
+  const void* c_in;           /* [n_tok][d_c] dtype c_dt: latent of each new token */
+  const void* k_in;           /* [n_tok][d_r] dtype k_dt: its rope key, NOT rotated */
+  const float* rms_gain;      /* [d_c] fp32 gain, or NULL for gain 1 (used iff normalize) */
+  const int32_t* seq;         /* [n_tok] sequence b of each new token */
+  const int32_t* pos;         /* [n_tok] its position s in the sequence */
+  const int32_t* block_table; /* [B][max_pages_per_seq] page ids, as for decode */
+  void* ckv;                  /* [n_pages][64][d_c] latent pool, dtype ckv_dt */
+  float* ckv_scale;           /* [n_pages][64] per-token scales iff ckv_dt == FP8_E4M3 */
+  void* kr;                   /* [n_pages][64][d_r] rotated-key pool, dtype kr_dt */
+} mla_append_args;
+
+/*
+ * mla_cache_append -- write n_tok new tokens into the paged pools.
+ * Token n goes to page block_table[seq[n]][pos[n] / 64], slot pos[n] % 64:
+ *   c = c_in[n]; if normalize:
+ *       c_j = c_j / sqrt(sum_j c_j^2 / 512 + rms_eps) * gain_j       (fp32)
+ *   ckv[page][slot] = c stored as ckv_dt:
+ *       F32 as is; BF16 rounded to nearest even;
+ *       FP8_E4M3: scale = fp32(max_j |c_j|) / 448 (fp32 division; 1 when
+ *       every c_j is 0), code_j = E4M3FN(fp32(c_j / scale)) rounded to
+ *       nearest even and saturated at +-448, ckv_scale[page][slot] = scale
+ *   kr[page][slot] = k_in[n] rotated at pos[n] (pairs (2i, 2i+1), angle,
+ *       cos, sin and rotation in fp64, rounded to fp32, then to bf16 for a
+ *       BF16 pool), as mla_rope computes it.
+ * With normalize = 0 and finite inputs the stored latent codes and scales
+ * are exactly those of the rule above. A token whose seq, position or page
+ * id is out of range writes nothing. Two tokens that address the same slot
+ * race (the result is one of them, unspecified). Inputs must be finite.
+ */
+int mla_cache_append(const mla_append_args* args, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

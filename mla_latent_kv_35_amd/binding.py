@@ -56,6 +56,22 @@ class DecodeArgs(ctypes.Structure):
     ]
 
 
+class AppendArgs(ctypes.Structure):
+    """Mirror of mla_append_args (include/mla.h)."""
+    _fields_ = [
+        ("n_tok", ctypes.c_int32), ("B", ctypes.c_int32),
+        ("d_c", ctypes.c_int32), ("d_r", ctypes.c_int32), ("page_size", ctypes.c_int32),
+        ("n_pages", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32),
+        ("c_dt", ctypes.c_int32), ("k_dt", ctypes.c_int32),
+        ("ckv_dt", ctypes.c_int32), ("kr_dt", ctypes.c_int32),
+        ("normalize", ctypes.c_int32), ("rms_eps", ctypes.c_float), ("reserved0", ctypes.c_int32),
+        ("rope_base", ctypes.c_double),
+        ("c_in", ctypes.c_void_p), ("k_in", ctypes.c_void_p), ("rms_gain", ctypes.c_void_p),
+        ("seq", ctypes.c_void_p), ("pos", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
+        ("ckv", ctypes.c_void_p), ("ckv_scale", ctypes.c_void_p), ("kr", ctypes.c_void_p),
+    ]
+
+
 _vp, _i, _d = ctypes.c_void_p, ctypes.c_int, ctypes.c_double
 _lib.mla_status_str.restype = ctypes.c_char_p
 _lib.mla_status_str.argtypes = [_i]
@@ -69,11 +85,13 @@ _lib.mla_decode_plan.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.POINTER(_i),
                                  ctypes.POINTER(_i), ctypes.POINTER(ctypes.c_size_t)]
 _lib.mla_decode_paged.restype = _i
 _lib.mla_decode_paged.argtypes = [ctypes.POINTER(DecodeArgs), _vp]
+_lib.mla_cache_append.restype = _i
+_lib.mla_cache_append.argtypes = [ctypes.POINTER(AppendArgs), _vp]
 _lib.mla_out_proj.restype = _i
 _lib.mla_out_proj.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]
 
 EXPORTED = ["mla_status_str", "mla_abi_version", "mla_absorb_q", "mla_rope",
-            "mla_decode_plan", "mla_decode_paged", "mla_out_proj"]
+            "mla_decode_plan", "mla_decode_paged", "mla_out_proj", "mla_cache_append"]
 
 
 def lib():
@@ -194,6 +212,25 @@ def make_decode_args(q_lat, q_rope, cache: PagedCache, T: int, softmax_scale: fl
     a.softmax_scale = softmax_scale
     a.reserved0 = 0
     return a
+
+
+def cache_append(cache: PagedCache, c_in: torch.Tensor, k_in: torch.Tensor, seq: torch.Tensor,
+                 pos: torch.Tensor, normalize: bool = False, rms_gain: Optional[torch.Tensor] = None,
+                 rms_eps: float = 0.0, rope_base: float = 10000.0, stream=None) -> None:
+    """Write new tokens (latent c_in [n, 512], unrotated key k_in [n, 64], at
+    sequence seq[n] and position pos[n]) into the cache's pools in place."""
+    n = c_in.shape[0]
+    a = AppendArgs()
+    a.n_tok, a.B = n, cache.block_table.shape[0]
+    a.d_c, a.d_r, a.page_size = c_in.shape[1], k_in.shape[1], PAGE_SIZE
+    a.n_pages, a.max_pages_per_seq = cache.n_pages, cache.block_table.shape[1]
+    a.c_dt, a.k_dt = dtype_code(c_in), dtype_code(k_in)
+    a.ckv_dt, a.kr_dt = dtype_code(cache.ckv), dtype_code(cache.kr)
+    a.normalize, a.rms_eps, a.reserved0, a.rope_base = int(normalize), rms_eps, 0, rope_base
+    a.c_in, a.k_in, a.rms_gain = _ptr(c_in), _ptr(k_in), _ptr(rms_gain)
+    a.seq, a.pos, a.block_table = _ptr(seq), _ptr(pos), _ptr(cache.block_table)
+    a.ckv, a.ckv_scale, a.kr = _ptr(cache.ckv), _ptr(cache.ckv_scale), _ptr(cache.kr)
+    _check("mla_cache_append", _lib.mla_cache_append(ctypes.byref(a), _stream(stream)))
 
 
 def decode_plan(args: DecodeArgs):

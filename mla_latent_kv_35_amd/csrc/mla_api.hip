@@ -228,4 +228,50 @@ int mla_out_proj(const void* u, const void* w_uv, void* o, int u_dt, int w_dt, i
   return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
 }
 
+int mla_cache_append(const mla_append_args* a, void* stream) {
+  if (!a) return MLA_ERR_NULL;
+  if (a->n_tok < 0 || a->B < 1 || a->n_pages < 1 || a->max_pages_per_seq < 1 || a->reserved0 != 0)
+    return MLA_ERR_SHAPE;
+  if (a->d_c != kDc || a->d_r != kDr || a->page_size != kPage) return MLA_ERR_UNSUPPORTED;
+  if (!is_float_dt(a->c_dt) || !is_float_dt(a->k_dt) || !is_float_dt(a->kr_dt) ||
+      !(is_float_dt(a->ckv_dt) || a->ckv_dt == MLA_FP8_E4M3))
+    return MLA_ERR_DTYPE;
+  if (a->normalize != 0 && a->normalize != 1) return MLA_ERR_SHAPE;
+  if (!(a->rms_eps >= 0.f) || !isfinite(a->rms_eps)) return MLA_ERR_SHAPE;
+  if (!(a->rope_base > 0.0) || !isfinite(a->rope_base)) return MLA_ERR_SHAPE;
+  if ((int64_t)a->max_pages_per_seq * kPage > INT32_MAX) return MLA_ERR_SHAPE;
+  if (a->n_tok == 0) return MLA_OK;
+  if (!a->c_in || !a->k_in || !a->seq || !a->pos || !a->block_table || !a->ckv || !a->kr)
+    return MLA_ERR_NULL;
+  if (a->ckv_dt == MLA_FP8_E4M3 && !a->ckv_scale) return MLA_ERR_NULL;
+  // the latent rows are read and written with 16-byte (8-byte for fp8) vector accesses
+  const uintptr_t al = (uintptr_t)a->c_in | (uintptr_t)a->ckv;
+  if (al % (a->ckv_dt == MLA_FP8_E4M3 ? 8 : 16) != 0 || (uintptr_t)a->c_in % 16 != 0 ||
+      ((uintptr_t)a->k_in | (uintptr_t)a->kr) % 4 != 0)
+    return MLA_ERR_UNSUPPORTED;
+  AppendParams p{};
+  p.c_in = a->c_in;
+  p.k_in = a->k_in;
+  p.rms_gain = a->rms_gain;
+  p.seq = a->seq;
+  p.pos = a->pos;
+  p.block_table = a->block_table;
+  p.ckv = a->ckv;
+  p.ckv_scale = a->ckv_scale;
+  p.kr = a->kr;
+  p.n_tok = a->n_tok;
+  p.B = a->B;
+  p.n_pages = a->n_pages;
+  p.max_pages = a->max_pages_per_seq;
+  p.c_bf16 = a->c_dt == MLA_BF16;
+  p.k_bf16 = a->k_dt == MLA_BF16;
+  p.kr_bf16 = a->kr_dt == MLA_BF16;
+  p.ckv_dt = a->ckv_dt == MLA_F32 ? 0 : a->ckv_dt == MLA_BF16 ? 1 : 2;
+  p.normalize = a->normalize;
+  p.rms_eps = a->rms_eps;
+  p.rope_base = a->rope_base;
+  const hipError_t e = launch_append(p, (hipStream_t)stream);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
+}
+
 }  // extern "C"

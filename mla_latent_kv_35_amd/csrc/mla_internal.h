@@ -55,6 +55,25 @@ struct CombineParams {
   int out_bf16;
 };
 
+struct AppendParams {
+  const void* c_in;         // [n_tok][512] f32 or bf16
+  const void* k_in;         // [n_tok][64] f32 or bf16 (not rotated)
+  const float* rms_gain;    // [512] or null
+  const int32_t* seq;       // [n_tok]
+  const int32_t* pos;       // [n_tok]
+  const int32_t* block_table;
+  void* ckv;                // [n_pages][64][512]
+  float* ckv_scale;         // [n_pages][64] (fp8 only)
+  void* kr;                 // [n_pages][64][64]
+  int n_tok, B, n_pages, max_pages;
+  int c_bf16, k_bf16, kr_bf16;
+  int ckv_dt;               // 0 f32, 1 bf16, 2 fp8 E4M3FN
+  int normalize;
+  float rms_eps;
+  double rope_base;
+};
+
+hipError_t launch_append(const AppendParams& p, hipStream_t s);
 hipError_t launch_decode_mfma_bf16(const DecodeParams& p, hipStream_t s);
 hipError_t launch_decode_mfma_fp8(const DecodeParams& p, hipStream_t s);
 hipError_t launch_decode_simple_f32(const DecodeParams& p, hipStream_t s);

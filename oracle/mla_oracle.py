@@ -26,6 +26,12 @@ analysis"):
   u_i = sum_s a_{s,i} c_s, and only then applies its own W^UV -- V2 analysis
   page, section 6.1 (per-head aggregation before B_i; the B_i cannot be summed
   across heads).
+* Cache append: each new token's latent (RMS-normalized, section 1.2) and its
+  rope key rotated at the token's position join the paged cache -- V2
+  analysis page, section 1.3, the token walk-through in section 6.3, and
+  section 6 (the key is cached already rotated). The fp8 storage follows the
+  per-token absmax/448 scale reading; its codes are chosen from the table of
+  E4M3FN values.
 * Explicit form: expand K = [W^UK c ; k^R] and V = W^UV c per head and run
   standard multi-head attention; it must equal the absorbed form up to
   rounding -- V2 analysis page, section 6.1 (training/prefill paragraph and
@@ -118,6 +124,98 @@ def rope_rotate(x: np.ndarray, pos: np.ndarray, base: float = 10000.0) -> np.nda
     out[..., 0::2] = x0 * c - x1 * s
     out[..., 1::2] = x0 * s + x1 * c
     return out
+
+
+# ----------------------------------------------------------------------------
+# Cache append: the 512 latent + 64 rotated rope elements of each new token
+# join the cache (V2 analysis page, section 1.3 and the token walk-through of
+# section 6.3); the latent is RMS-normalized after the down-projection
+# (section 1.2); the rope key is cached already rotated (section 6).
+# ----------------------------------------------------------------------------
+
+
+def rms_normalize(c: np.ndarray, gain: Optional[np.ndarray] = None, eps: float = 0.0) -> np.ndarray:
+    """RMSNorm of each row: c / sqrt(mean(c^2) + eps) * gain, in float64
+    (V2 analysis page, section 1.2; the gain is not given there, so it is an
+    input, 1 when absent)."""
+    c = np.asarray(c, dtype=np.float64)
+    r = np.sqrt(np.mean(c * c, axis=-1, keepdims=True) + eps)
+    out = c / r
+    if gain is not None:
+        out = out * np.asarray(gain, dtype=np.float32).astype(np.float64)
+    return out
+
+
+def f64_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round to binary32 (nearest even), then keep the upper 16 bits rounded to
+    nearest even on the lower 16 (finite values)."""
+    x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
+    u = np.ascontiguousarray(x32).view(np.uint32).astype(np.uint64)
+    r = (u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)
+    return r.astype(np.uint16)
+
+
+def e4m3fn_round(y: np.ndarray) -> np.ndarray:
+    """binary32 values -> E4M3FN codes: the nearest finite E4M3FN value, ties to
+    the even code (even mantissa), magnitudes above 448 saturated to 448.
+    Chosen from the table of all finite values (e4m3fn_to_f64)."""
+    vals = e4m3fn_to_f64(np.arange(0x7F, dtype=np.uint8))     # codes 0..0x7E: 0 .. 448
+    yf = np.asarray(y, dtype=np.float32)
+    a = np.minimum(np.abs(yf.astype(np.float64)), 448.0)
+    hi = np.clip(np.searchsorted(vals, a, side="left"), 0, 0x7E)
+    lo = np.maximum(hi - 1, 0)
+    d_lo, d_hi = a - vals[lo], vals[hi] - a
+    code = np.where((d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0)), hi, lo)
+    return (code | np.where(np.signbit(yf), 0x80, 0)).astype(np.uint8)
+
+
+def quantize_fp8_token(c32: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Per-token E4M3FN quantization with one fp32 scale, decided in binary32:
+    scale = fp32(max_j |c_j|) / 448 (binary32 division; 1 for an all-zero row),
+    code_j = E4M3FN(fp32(c_j / scale))."""
+    c32 = np.asarray(c32, dtype=np.float32)
+    amax = np.abs(c32).max(axis=-1)
+    scale = (amax / np.float32(448.0)).astype(np.float32)
+    scale = np.where(amax == 0, np.float32(1.0), scale).astype(np.float32)
+    y = (c32 / scale[..., None]).astype(np.float32)
+    return e4m3fn_round(y), scale
+
+
+def cache_append(pools: Dict[str, np.ndarray], c_in: np.ndarray, c_dt: str, k_in: np.ndarray,
+                 k_dt: str, seq: np.ndarray, pos: np.ndarray, block_table: np.ndarray,
+                 ckv_dt: str, kr_dt: str, normalize: bool = False,
+                 gain: Optional[np.ndarray] = None, eps: float = 0.0,
+                 rope_base: float = 10000.0) -> None:
+    """Write each new token into pools["ckv"], pools["kr"] (and pools["scale"]
+    for fp8) in place: token n goes to page block_table[seq[n]][pos[n] // 64],
+    slot pos[n] % 64; tokens whose sequence, position or page id is out of
+    range are skipped. Latent: optional RMSNorm (float64), then stored as f32
+    (rounded once), bf16 (via binary32) or fp8 (quantize_fp8_token of its
+    binary32 value). Key: rotated at pos[n] in float64 (rope_rotate), rounded
+    to binary32 and, for a bf16 pool, to bf16."""
+    B, max_pages = block_table.shape
+    n_pages = pools["ckv"].shape[0]
+    for n in range(len(seq)):
+        b, s = int(seq[n]), int(pos[n])
+        if not (0 <= b < B and 0 <= s < max_pages * PAGE):
+            continue
+        page = int(block_table[b, s // PAGE])
+        if not (0 <= page < n_pages):
+            continue
+        slot = s % PAGE
+        c = stored_to_f64(c_in[n], c_dt)
+        if normalize:
+            c = rms_normalize(c, gain, eps)
+        if ckv_dt == "f32":
+            pools["ckv"][page, slot] = c.astype(np.float32)
+        elif ckv_dt == "bf16":
+            pools["ckv"][page, slot] = f64_to_bf16_bits(c)
+        else:
+            codes, sc = quantize_fp8_token(c.astype(np.float32))
+            pools["ckv"][page, slot] = codes
+            pools["scale"][page, slot] = sc
+        k = rope_rotate(stored_to_f64(k_in[n], k_dt)[None, :], np.array([s]), rope_base)[0]
+        pools["kr"][page, slot] = k.astype(np.float32) if kr_dt == "f32" else f64_to_bf16_bits(k)
 
 
 def absorb_q(q_nope: np.ndarray, w_uk: np.ndarray) -> np.ndarray:

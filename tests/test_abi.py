@@ -112,3 +112,42 @@ def test_dense_entry_points_reject_before_launch(B):
     assert L.mla_rope(None, None, 1, None, 4, 128, 64, 10000.0, None) == 1
     assert L.mla_out_proj(None, None, None, 1, 0, 1, 4, 128, 128, 512, None) == 3
     assert L.mla_out_proj(None, None, None, 1, 1, 1, -1, 128, 128, 512, None) == 2
+
+
+def _append_args(mod, **kw):
+    a = mod.AppendArgs()
+    a.n_tok, a.B, a.d_c, a.d_r, a.page_size = 4, 2, 512, 64, 64
+    a.n_pages, a.max_pages_per_seq = 8, 4
+    a.c_dt = a.k_dt = a.ckv_dt = a.kr_dt = mod.MLA_BF16
+    a.normalize, a.rms_eps, a.reserved0, a.rope_base = 0, 0.0, 0, 10000.0
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("n_tok", -1, 2), ("B", 0, 2), ("n_pages", 0, 2), ("max_pages_per_seq", 0, 2),
+    ("reserved0", 1, 2), ("d_c", 256, 4), ("d_r", 32, 4), ("page_size", 16, 4),
+    ("c_dt", 2, 3), ("k_dt", 2, 3), ("kr_dt", 2, 3), ("ckv_dt", 5, 3),
+    ("normalize", 2, 2), ("rms_eps", -1.0, 2), ("rms_eps", float("inf"), 2),
+    ("rope_base", 0.0, 2), ("max_pages_per_seq", 1 << 26, 2),
+])
+def test_append_rejects_bad_arguments(B, field, value, status):
+    assert B.lib().mla_cache_append(ctypes.byref(_append_args(B, **{field: value})), None) == status
+
+
+def test_append_rejects_before_launch(B):
+    L = B.lib()
+    assert L.mla_cache_append(None, None) == 1
+    a = _append_args(B)
+    assert L.mla_cache_append(ctypes.byref(a), None) == 1          # null tensors
+    a.n_tok = 0
+    assert L.mla_cache_append(ctypes.byref(a), None) == 0          # empty: no-op
+    fake = 0x1000
+    a = _append_args(B, ckv_dt=B.MLA_FP8_E4M3)
+    for name in ("c_in", "k_in", "seq", "pos", "block_table", "ckv", "kr"):
+        setattr(a, name, fake)
+    assert L.mla_cache_append(ctypes.byref(a), None) == 1          # fp8 without scales
+    a.ckv_dt = B.MLA_BF16
+    a.c_in = fake + 8                                              # misaligned latent rows
+    assert L.mla_cache_append(ctypes.byref(a), None) == 4
