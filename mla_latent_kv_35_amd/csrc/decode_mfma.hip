@@ -22,9 +22,12 @@
 //    (section 6.1). Between its MFMA groups it issues the asynchronous copies
 //    of tile j+2.
 //
-// Per step: barrier X (tile j resident, P(j-1) published), barrier Y (score
-// team's tile maxima published). Four tile buffers keep two tiles in flight
-// while two are in use. All barriers order LDS only; the page copies are
+// Per step one workgroup barrier, X (tile j resident, P(j-1) published).
+// The two score waves that split a row group's tokens exchange their tile
+// maxima through LDS: each writes its maxima, then a flag holding the step
+// number, and waits (bounded) for its partner's flag only, so neither the
+// other pair nor the aggregation team is held up. Four tile buffers keep two
+// tiles in flight while two are in use. All barriers order LDS only; the page copies are
 // waited for explicitly with vmcnt by the waves that issued them. Before
 // step 0 the absorbed queries pass through LDS once: each score wave loads
 // half of its rows' fragments and takes the other half from its partner
@@ -74,7 +77,8 @@ struct Geo {
   static constexpr int kStageBytes = 2 * 2 * 18 * 1024;
   static constexpr int kOffIds = (kOffM + 64 * 4 > kOffStage + kStageBytes) ? kOffM + 64 * 4
                                                                             : kOffStage + kStageBytes;
-  static constexpr int kLdsBytes = kOffIds + kMaxSplitPages * 4;
+  static constexpr int kOffFlags = kOffIds + kMaxSplitPages * 4;   // per score wave: last step synced
+  static constexpr int kLdsBytes = kOffFlags + 4 * 4;
   // page copies per tile per aggregation wave: bf16 8 latent rows + 1 rope
   // block; fp8 4 latent row pairs + 1 rope block (+ the scales on wave 0)
   static constexpr int kDma = FP8 ? 5 : 9;
@@ -248,6 +252,7 @@ void decode_mfma_kernel(DecodeParams p) {
   float* const redmax = (float*)(smem_raw + kOffRed);       // [2][64]
   float* const lsum = (float*)(smem_raw + kOffLsum);        // [2][64]
   float* const mbuf = (float*)(smem_raw + kOffM);           // [64]
+  MLA_LDS int* const flags = (MLA_LDS int*)(smem + Gm::kOffFlags);
   const char* const ckv_base = (const char*)p.ckv;
   const char* const kr_base = (const char*)p.kr;
 
@@ -301,6 +306,7 @@ void decode_mfma_kernel(DecodeParams p) {
     if (tok0 >= tok1) return;   // split past the end of the sequence: no partial
     if (th == 0) q_stage(std::integral_constant<int, 0>{});
     else q_stage(std::integral_constant<int, 1>{});
+    if (lane == 0) flags[w] = -1;
     lds_sync();  // (Q) both halves staged
     if (th == 0) q_half(std::integral_constant<int, 1>{}, true);
     else q_half(std::integral_constant<int, 0>{}, true);
@@ -408,7 +414,18 @@ void decode_mfma_kernel(DecodeParams p) {
           if (lane < 16) redmax[th * 64 + 32 * hh + 16 * ht + lane] = mx[ht];
         }
       }
-      lds_sync();  // (Y) tile maxima of all rows visible
+      if (j < n_tiles) {
+        // the partner wave (other token half, same rows) instead of a
+        // workgroup barrier: this wave's maxima are in LDS before its flag
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        asm volatile("" ::: "memory");
+        if (lane == 0) *(volatile MLA_LDS int*)(flags + w) = j;
+        int it = 0;
+        while (__builtin_amdgcn_readfirstlane(*(volatile MLA_LDS int*)(flags + (w ^ 2))) != j &&
+               ++it < (1 << 20))
+          __builtin_amdgcn_s_sleep(1);
+        asm volatile("" ::: "memory");
+      }
       if (j < n_tiles) {
         lds_char* const pj = pbuf + (j & 1) * kPBytes;
         float* const aj = alphabuf + (j & 1) * 64;
@@ -639,7 +656,6 @@ void decode_mfma_kernel(DecodeParams p) {
       }
       pv_half(tile, 0, more, src);
     }
-    lds_sync();  // (Y)
     if (j >= 1) pv_half(tile, 1, more, src);
     // tile j+1 must be resident at the next (X); tile j+2's copies may fly on
     wait_tile(more);
