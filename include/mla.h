@@ -93,6 +93,46 @@ int mla_rope(const void* x_in, void* x_out, int dt, const int32_t* pos,
              int n_tok, int n_heads, int d_r, double base, void* stream);
 
 /*
+ * mla_rope_freq -- mla_rope with caller-given per-pair frequencies:
+ *   a = pos[n] * theta[i]   (fp64), then the same rotation as mla_rope.
+ *   theta : DEVICE fp64 [d_r / 2], e.g. from mla_yarn_frequencies.
+ * Same layouts, support and errors as mla_rope (theta NULL: MLA_ERR_NULL).
+ */
+int mla_rope_freq(const void* x_in, void* x_out, int dt, const int32_t* pos,
+                  int n_tok, int n_heads, int d_r, const double* theta, void* stream);
+
+/*
+ * mla_yarn_frequencies -- YaRN frequencies of the decoupled rope part for a
+ * context extended by `factor` (V2 analysis page, section 3.2: YaRN acts on
+ * the 64 rope dimensions only; V2 uses factor s = 40, alpha = 1, beta = 32 on
+ * a 4K original window). The pages do not print the interpolation rule; this
+ * is the NTK-by-parts ramp of the YaRN method, per pair i:
+ *   theta_i  = base^(-2i/d_r),  r_i = orig_len * theta_i / (2 pi)
+ *              (rotations of pair i over the original window)
+ *   gamma_i  = clamp((r_i - alpha) / (beta - alpha), 0, 1)
+ *   theta'_i = (1 - gamma_i) * theta_i / factor + gamma_i * theta_i
+ * so pairs that turn fewer than alpha times are fully interpolated, pairs
+ * that turn more than beta times are unchanged. factor = 1 gives theta_i.
+ *   theta : HOST fp64 [d_r / 2], written.
+ * Errors: MLA_ERR_NULL (theta), MLA_ERR_SHAPE (d_r odd or outside 2..256,
+ * base <= 0, factor < 1, beta <= alpha, orig_len < 1).
+ */
+int mla_yarn_frequencies(int d_r, double base, double factor, double alpha, double beta,
+                         int orig_len, double* theta);
+
+/*
+ * mla_yarn_mscale -- YaRN attention temperature factor sqrt(1/t) =
+ * coef * ln(factor) + 1 (1 for factor <= 1). V2 analysis page, section 3.2:
+ * V2 uses coef = 0.0707 (about 1.26 at factor 40; the original YaRN
+ * coefficient 0.1 gives about 1.37), applied through the softmax scale
+ * rather than the rope cos/sin, because only the 64 rope dimensions of MLA
+ * are rotated. The original scheme scales q and k each by sqrt(1/t), i.e.
+ * the logits by 1/t, so the softmax scale to pass to mla_decode_paged is
+ * 1/sqrt(d_h + d_r) * mla_yarn_mscale(factor, coef)^2.
+ */
+double mla_yarn_mscale(double factor, double coef);
+
+/*
  * Arguments of the paged absorbed-decode kernel.
  *
  * Paged cache: token s of sequence b lives in page block_table[b][s / 64],
@@ -198,6 +238,8 @@ typedef struct mla_append_args {
   float rms_eps;              /* RMSNorm epsilon (>= 0, finite) */
   int32_t reserved0;          /* must be 0 */
   double rope_base;           /* > 0; angles pos * base^(-2i/64), as mla_rope */
+  const double* rope_theta;   /* DEVICE fp64 [d_r / 2] per-pair frequencies (e.g. YaRN,
+                                 mla_yarn_frequencies), or NULL for base^(-2i/64) */
   const void* c_in;           /* [n_tok][d_c] dtype c_dt: latent of each new token */
   const void* k_in;           /* [n_tok][d_r] dtype k_dt: its rope key, NOT rotated */
   const float* rms_gain;      /* [d_c] fp32 gain, or NULL for gain 1 (used iff normalize) */
@@ -221,7 +263,8 @@ typedef struct mla_append_args {
  *       nearest even and saturated at +-448, ckv_scale[page][slot] = scale
  *   kr[page][slot] = k_in[n] rotated at pos[n] (pairs (2i, 2i+1), angle,
  *       cos, sin and rotation in fp64, rounded to fp32, then to bf16 for a
- *       BF16 pool), as mla_rope computes it.
+ *       BF16 pool), as mla_rope computes it (mla_rope_freq when rope_theta
+ *       is given).
  * With normalize = 0 and finite inputs the stored latent codes and scales
  * are exactly those of the rule above. A token whose seq, position or page
  * id is out of range writes nothing. Two tokens that address the same slot

@@ -65,7 +65,7 @@ class AppendArgs(ctypes.Structure):
         ("c_dt", ctypes.c_int32), ("k_dt", ctypes.c_int32),
         ("ckv_dt", ctypes.c_int32), ("kr_dt", ctypes.c_int32),
         ("normalize", ctypes.c_int32), ("rms_eps", ctypes.c_float), ("reserved0", ctypes.c_int32),
-        ("rope_base", ctypes.c_double),
+        ("rope_base", ctypes.c_double), ("rope_theta", ctypes.c_void_p),
         ("c_in", ctypes.c_void_p), ("k_in", ctypes.c_void_p), ("rms_gain", ctypes.c_void_p),
         ("seq", ctypes.c_void_p), ("pos", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
         ("ckv", ctypes.c_void_p), ("ckv_scale", ctypes.c_void_p), ("kr", ctypes.c_void_p),
@@ -85,13 +85,20 @@ _lib.mla_decode_plan.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.POINTER(_i),
                                  ctypes.POINTER(_i), ctypes.POINTER(ctypes.c_size_t)]
 _lib.mla_decode_paged.restype = _i
 _lib.mla_decode_paged.argtypes = [ctypes.POINTER(DecodeArgs), _vp]
+_lib.mla_rope_freq.restype = _i
+_lib.mla_rope_freq.argtypes = [_vp, _vp, _i, _vp, _i, _i, _i, _vp, _vp]
+_lib.mla_yarn_frequencies.restype = _i
+_lib.mla_yarn_frequencies.argtypes = [_i, _d, _d, _d, _d, _i, ctypes.POINTER(_d)]
+_lib.mla_yarn_mscale.restype = _d
+_lib.mla_yarn_mscale.argtypes = [_d, _d]
 _lib.mla_cache_append.restype = _i
 _lib.mla_cache_append.argtypes = [ctypes.POINTER(AppendArgs), _vp]
 _lib.mla_out_proj.restype = _i
 _lib.mla_out_proj.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]
 
 EXPORTED = ["mla_status_str", "mla_abi_version", "mla_absorb_q", "mla_rope",
-            "mla_decode_plan", "mla_decode_paged", "mla_out_proj", "mla_cache_append"]
+            "mla_decode_plan", "mla_decode_paged", "mla_out_proj", "mla_cache_append",
+            "mla_rope_freq", "mla_yarn_frequencies", "mla_yarn_mscale"]
 
 
 def lib():
@@ -158,6 +165,31 @@ def rope(x: torch.Tensor, pos: torch.Tensor, base: float = 10000.0,
     return out
 
 
+def rope_freq(x: torch.Tensor, pos: torch.Tensor, theta: torch.Tensor,
+              out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """mla_rope with per-pair frequencies theta (device float64 [d_r/2])."""
+    n, heads, dr = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    assert theta.dtype == torch.float64 and theta.numel() == dr // 2
+    _check("mla_rope_freq", _lib.mla_rope_freq(_ptr(x), _ptr(out), dtype_code(x), _ptr(pos), n,
+                                               heads, dr, _ptr(theta), _stream(stream)))
+    return out
+
+
+def yarn_frequencies(d_r: int = 64, base: float = 10000.0, factor: float = 40.0,
+                     alpha: float = 1.0, beta: float = 32.0, orig_len: int = 4096) -> np.ndarray:
+    """Host float64 [d_r/2] YaRN frequencies (mla_yarn_frequencies)."""
+    out = (ctypes.c_double * (d_r // 2))()
+    _check("mla_yarn_frequencies", _lib.mla_yarn_frequencies(d_r, base, factor, alpha, beta,
+                                                             orig_len, out))
+    return np.array(out[:], dtype=np.float64)
+
+
+def yarn_mscale(factor: float = 40.0, coef: float = 0.0707) -> float:
+    return _lib.mla_yarn_mscale(factor, coef)
+
+
 def out_proj(u: torch.Tensor, w_uv: torch.Tensor, out_dtype=None,
              out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """o[n,h,:] = W_UV[h] u[n,h,:]; u [n,H,512], w_uv [H,128,512]."""
@@ -216,7 +248,8 @@ def make_decode_args(q_lat, q_rope, cache: PagedCache, T: int, softmax_scale: fl
 
 def cache_append(cache: PagedCache, c_in: torch.Tensor, k_in: torch.Tensor, seq: torch.Tensor,
                  pos: torch.Tensor, normalize: bool = False, rms_gain: Optional[torch.Tensor] = None,
-                 rms_eps: float = 0.0, rope_base: float = 10000.0, stream=None) -> None:
+                 rms_eps: float = 0.0, rope_base: float = 10000.0,
+                 rope_theta: Optional[torch.Tensor] = None, stream=None) -> None:
     """Write new tokens (latent c_in [n, 512], unrotated key k_in [n, 64], at
     sequence seq[n] and position pos[n]) into the cache's pools in place."""
     n = c_in.shape[0]
@@ -227,6 +260,7 @@ def cache_append(cache: PagedCache, c_in: torch.Tensor, k_in: torch.Tensor, seq:
     a.c_dt, a.k_dt = dtype_code(c_in), dtype_code(k_in)
     a.ckv_dt, a.kr_dt = dtype_code(cache.ckv), dtype_code(cache.kr)
     a.normalize, a.rms_eps, a.reserved0, a.rope_base = int(normalize), rms_eps, 0, rope_base
+    a.rope_theta = _ptr(rope_theta)
     a.c_in, a.k_in, a.rms_gain = _ptr(c_in), _ptr(k_in), _ptr(rms_gain)
     a.seq, a.pos, a.block_table = _ptr(seq), _ptr(pos), _ptr(cache.block_table)
     a.ckv, a.ckv_scale, a.kr = _ptr(cache.ckv), _ptr(cache.ckv_scale), _ptr(cache.kr)

@@ -128,7 +128,8 @@ __global__ __launch_bounds__(64 * kTokPerBlock) void append_kernel(AppendParams 
       x0 = src[0];
       x1 = src[1];
     }
-    const double theta = pow(p.rope_base, -2.0 * (double)lane / (double)kDr);
+    const double theta =
+        p.rope_theta ? p.rope_theta[lane] : pow(p.rope_base, -2.0 * (double)lane / (double)kDr);
     double sn, cn;
     sincos((double)s * theta, &sn, &cn);
     const float y0 = (float)(x0 * cn - x1 * sn);

@@ -132,8 +132,42 @@ int mla_rope(const void* x_in, void* x_out, int dt, const int32_t* pos, int n_to
   if (n_tok == 0) return MLA_OK;
   if (!x_in || !x_out || !pos) return MLA_ERR_NULL;
   const hipError_t e = launch_rope(x_in, x_out, dt == MLA_BF16, pos, n_tok, n_heads, d_r, base,
-                                   (hipStream_t)stream);
+                                   nullptr, (hipStream_t)stream);
   return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
+}
+
+int mla_rope_freq(const void* x_in, void* x_out, int dt, const int32_t* pos, int n_tok,
+                  int n_heads, int d_r, const double* theta, void* stream) {
+  if (n_tok < 0 || n_heads < 1) return MLA_ERR_SHAPE;
+  if (d_r < 2 || d_r > 256 || d_r % 2 != 0) return MLA_ERR_UNSUPPORTED;
+  if (!is_float_dt(dt)) return MLA_ERR_DTYPE;
+  if (n_tok == 0) return MLA_OK;
+  if (!x_in || !x_out || !pos || !theta) return MLA_ERR_NULL;
+  const hipError_t e = launch_rope(x_in, x_out, dt == MLA_BF16, pos, n_tok, n_heads, d_r, 1.0,
+                                   theta, (hipStream_t)stream);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
+}
+
+int mla_yarn_frequencies(int d_r, double base, double factor, double alpha, double beta,
+                         int orig_len, double* theta) {
+  if (!theta) return MLA_ERR_NULL;
+  if (d_r < 2 || d_r > 256 || d_r % 2 != 0) return MLA_ERR_SHAPE;
+  if (!(base > 0.0) || !isfinite(base) || !(factor >= 1.0) || !isfinite(factor) ||
+      !(beta > alpha) || !isfinite(alpha) || !isfinite(beta) || orig_len < 1)
+    return MLA_ERR_SHAPE;
+  const double two_pi = 6.283185307179586476925286766559;
+  for (int i = 0; i < d_r / 2; ++i) {
+    const double th = pow(base, -2.0 * (double)i / (double)d_r);
+    const double r = (double)orig_len * th / two_pi;     // rotations over the original window
+    double g = (r - alpha) / (beta - alpha);
+    g = g < 0.0 ? 0.0 : (g > 1.0 ? 1.0 : g);
+    theta[i] = (1.0 - g) * (th / factor) + g * th;
+  }
+  return MLA_OK;
+}
+
+double mla_yarn_mscale(double factor, double coef) {
+  return factor <= 1.0 ? 1.0 : coef * log(factor) + 1.0;
 }
 
 int mla_decode_plan(const mla_decode_args* args, int* split_tokens, int* n_split,
@@ -270,6 +304,7 @@ int mla_cache_append(const mla_append_args* a, void* stream) {
   p.normalize = a->normalize;
   p.rms_eps = a->rms_eps;
   p.rope_base = a->rope_base;
+  p.rope_theta = a->rope_theta;
   const hipError_t e = launch_append(p, (hipStream_t)stream);
   return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
 }

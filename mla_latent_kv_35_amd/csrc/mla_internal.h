@@ -71,6 +71,7 @@ struct AppendParams {
   int normalize;
   float rms_eps;
   double rope_base;
+  const double* rope_theta; // [32] or null (base^(-2i/64))
 };
 
 hipError_t launch_append(const AppendParams& p, hipStream_t s);
@@ -79,8 +80,9 @@ hipError_t launch_decode_mfma_fp8(const DecodeParams& p, hipStream_t s);
 hipError_t launch_decode_simple_f32(const DecodeParams& p, hipStream_t s);
 hipError_t launch_combine(const CombineParams& p, hipStream_t s);
 
+// theta: device fp64 [d_r/2] per-pair frequencies, or null for base^(-2i/d_r)
 hipError_t launch_rope(const void* x_in, void* x_out, int bf16, const int32_t* pos, int n_tok,
-                       int n_heads, int d_r, double base, hipStream_t s);
+                       int n_heads, int d_r, double base, const double* theta, hipStream_t s);
 hipError_t launch_absorb(const void* q_nope, const void* w_uk, void* q_lat, int in_bf16,
                          int out_bf16, int n_tok, int H, hipStream_t s);
 hipError_t launch_out_proj(const void* u, const void* w_uv, void* o, int u_bf16, int w_bf16,

@@ -23,7 +23,7 @@ constexpr int kHeadsPerBlock = 32;
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void rope64_kernel(const void* x_in, void* x_out,
                                                           const int32_t* pos, int n_heads,
-                                                          double base) {
+                                                          double base, const double* freq) {
   __shared__ double cs[32][2];
   const int n = blockIdx.x;
   const int h0 = blockIdx.y * kHeadsPerBlock;
@@ -43,7 +43,7 @@ __global__ __launch_bounds__(kThreads) void rope64_kernel(const void* x_in, void
     if (ok[q]) v[q] = *(const u32x4_t*)((const char*)x_in + off[q]);
   }
   if (tid < 32) {
-    const double theta = pow(base, -2.0 * (double)tid / 64.0);
+    const double theta = freq ? freq[tid] : pow(base, -2.0 * (double)tid / 64.0);
     double sn, cn;
     sincos((double)pos[n] * theta, &sn, &cn);
     cs[tid][0] = cn;
@@ -82,13 +82,13 @@ __global__ __launch_bounds__(kThreads) void rope64_kernel(const void* x_in, void
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void rope_kernel(const void* x_in, void* x_out,
                                                         const int32_t* pos, int n_heads, int d_r,
-                                                        double base) {
+                                                        double base, const double* freq) {
   __shared__ double cs[kMaxHalf][2];
   const int n = blockIdx.x;
   const int half = d_r / 2;
   const double pn = (double)pos[n];
   for (int i = threadIdx.x; i < half; i += kThreads) {
-    const double theta = pow(base, -2.0 * (double)i / (double)d_r);
+    const double theta = freq ? freq[i] : pow(base, -2.0 * (double)i / (double)d_r);
     double s, c;
     sincos(pn * theta, &s, &c);
     cs[i][0] = c;
@@ -123,23 +123,23 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(const void* x_in, void* 
 }  // namespace
 
 hipError_t launch_rope(const void* x_in, void* x_out, int bf16, const int32_t* pos, int n_tok,
-                       int n_heads, int d_r, double base, hipStream_t s) {
+                       int n_heads, int d_r, double base, const double* theta, hipStream_t s) {
   if (d_r == 64 && (((uintptr_t)x_in | (uintptr_t)x_out) & 15) == 0) {
     const dim3 grid(n_tok, (n_heads + kHeadsPerBlock - 1) / kHeadsPerBlock);
     if (bf16)
       hipLaunchKernelGGL(rope64_kernel<true>, grid, dim3(kThreads), 0, s, x_in, x_out, pos, n_heads,
-                         base);
+                         base, theta);
     else
       hipLaunchKernelGGL(rope64_kernel<false>, grid, dim3(kThreads), 0, s, x_in, x_out, pos,
-                         n_heads, base);
+                         n_heads, base, theta);
     return hipGetLastError();
   }
   if (bf16)
     hipLaunchKernelGGL(rope_kernel<true>, dim3(n_tok), dim3(kThreads), 0, s, x_in, x_out, pos,
-                       n_heads, d_r, base);
+                       n_heads, d_r, base, theta);
   else
     hipLaunchKernelGGL(rope_kernel<false>, dim3(n_tok), dim3(kThreads), 0, s, x_in, x_out, pos,
-                       n_heads, d_r, base);
+                       n_heads, d_r, base, theta);
   return hipGetLastError();
 }
 

@@ -97,8 +97,10 @@ def stored_to_f64(arr: np.ndarray, dt: str, scale: Optional[np.ndarray] = None) 
 # ----------------------------------------------------------------------------
 
 
-def rope_rotate(x: np.ndarray, pos: np.ndarray, base: float = 10000.0) -> np.ndarray:
-    """Rotate pairs (x[2i], x[2i+1]) by the angle pos * base^(-2i/d).
+def rope_rotate(x: np.ndarray, pos: np.ndarray, base: float = 10000.0,
+                theta: Optional[np.ndarray] = None) -> np.ndarray:
+    """Rotate pairs (x[2i], x[2i+1]) by the angle pos * base^(-2i/d), or by
+    pos * theta[i] when per-pair frequencies theta are given (YaRN).
 
     x: [..., n, d] (or [n, d]) float64; pos: [n] integer positions, one per
     leading row of x's second-to-last axis when x is [n, d], or broadcastable
@@ -108,7 +110,10 @@ def rope_rotate(x: np.ndarray, pos: np.ndarray, base: float = 10000.0) -> np.nda
     d = x.shape[-1]
     assert d % 2 == 0
     # theta_i = base^(-2i/d) from libm's pow, one value per pair
-    theta = np.array([math.pow(base, -2.0 * i / d) for i in range(d // 2)])
+    if theta is None:
+        theta = np.array([math.pow(base, -2.0 * i / d) for i in range(d // 2)])
+    theta = np.asarray(theta, dtype=np.float64)
+    assert theta.shape == (d // 2,)
     p = np.asarray(pos, dtype=np.int64)
     # cos/sin from libm (full-precision argument reduction: angles reach 1e5
     # rad at 128K positions), evaluated once per distinct position.
@@ -185,7 +190,7 @@ def cache_append(pools: Dict[str, np.ndarray], c_in: np.ndarray, c_dt: str, k_in
                  k_dt: str, seq: np.ndarray, pos: np.ndarray, block_table: np.ndarray,
                  ckv_dt: str, kr_dt: str, normalize: bool = False,
                  gain: Optional[np.ndarray] = None, eps: float = 0.0,
-                 rope_base: float = 10000.0) -> None:
+                 rope_base: float = 10000.0, theta: Optional[np.ndarray] = None) -> None:
     """Write each new token into pools["ckv"], pools["kr"] (and pools["scale"]
     for fp8) in place: token n goes to page block_table[seq[n]][pos[n] // 64],
     slot pos[n] % 64; tokens whose sequence, position or page id is out of
@@ -214,8 +219,35 @@ def cache_append(pools: Dict[str, np.ndarray], c_in: np.ndarray, c_dt: str, k_in
             codes, sc = quantize_fp8_token(c.astype(np.float32))
             pools["ckv"][page, slot] = codes
             pools["scale"][page, slot] = sc
-        k = rope_rotate(stored_to_f64(k_in[n], k_dt)[None, :], np.array([s]), rope_base)[0]
+        k = rope_rotate(stored_to_f64(k_in[n], k_dt)[None, :], np.array([s]), rope_base, theta)[0]
         pools["kr"][page, slot] = k.astype(np.float32) if kr_dt == "f32" else f64_to_bf16_bits(k)
+
+
+def yarn_theta(d: int, base: float, factor: float, alpha: float, beta: float,
+               orig_len: int) -> np.ndarray:
+    """YaRN frequencies of the rope part (V2 analysis page, section 3.2: YaRN
+    acts on the 64 decoupled rope dimensions only; V2 extends a 4K window by
+    factor 40 with alpha = 1, beta = 32). The pages refer elsewhere for the
+    interpolation rule; this is the YaRN method's ramp over the number of
+    turns r_i a pair makes across the original window: pairs with r_i <= alpha
+    are slowed by the factor, pairs with r_i >= beta keep their frequency,
+    pairs in between blend linearly."""
+    out = np.empty(d // 2)
+    for i in range(d // 2):
+        th = math.pow(base, -2.0 * i / d)
+        turns = orig_len * th / (2.0 * math.pi)
+        g = min(1.0, max(0.0, (turns - alpha) / (beta - alpha)))
+        out[i] = (1.0 - g) * (th / factor) + g * th
+    return out
+
+
+def yarn_mscale(factor: float, coef: float = 0.0707) -> float:
+    """YaRN temperature factor sqrt(1/t) = coef ln(factor) + 1 (V2 analysis
+    page, section 3.2: V2's coefficient is 0.0707, the original 0.1; the
+    report's sqrt(t) is a typo for sqrt(1/t)). The pages move it onto the
+    softmax scale; since the original scheme scales q and k each by it, the
+    logits scale by its square (this oracle's reading)."""
+    return 1.0 if factor <= 1.0 else coef * math.log(factor) + 1.0
 
 
 def absorb_q(q_nope: np.ndarray, w_uk: np.ndarray) -> np.ndarray:
@@ -335,15 +367,19 @@ def sequence_cache(inp, b: int) -> Tuple[np.ndarray, np.ndarray]:
 
 
 def decode_step(inp, batches: Optional[Iterable[int]] = None, rope_base: float = 10000.0,
-                split_tokens: Optional[int] = None):
+                split_tokens: Optional[int] = None, theta: Optional[np.ndarray] = None,
+                softmax_scale: Optional[float] = None):
     """The whole absorbed decode step for the chosen sequences.
 
     Returns dict of float64 arrays indexed by sequence b:
     q_lat [T, H, d_c], q_rot [T, H, d_r], u [T, H, d_c], lse [T, H],
     o [T, H, d_h]. With split_tokens set, each sequence is computed split by
     split and merged with combine_partials (for the split/combine pins).
+    theta: per-pair rope frequencies for the query (YaRN); softmax_scale:
+    replaces 1/sqrt(d_h + d_R) (YaRN temperature).
     """
     cfg = inp.cfg
+    scale = cfg.softmax_scale if softmax_scale is None else softmax_scale
     T, H = cfg.T, cfg.H
     dec = decoded_inputs(inp)
     res = {}
@@ -351,17 +387,17 @@ def decode_step(inp, batches: Optional[Iterable[int]] = None, rope_base: float =
         rows = slice(b * T, (b + 1) * T)
         q_lat = absorb_q(dec["q_nope"][rows], dec["w_uk"])                  # [T, H, d_c]
         pos = np.asarray(inp.positions[rows], dtype=np.int64)
-        q_rot = rope_rotate(dec["q_rope"][rows], pos, rope_base)            # [T, H, d_r]
+        q_rot = rope_rotate(dec["q_rope"][rows], pos, rope_base, theta)     # [T, H, d_r]
         C, KR = sequence_cache(inp, b)
         L = C.shape[0]
         visible = np.repeat(pos + 1, H)                                     # row (t,h) sees s <= pos_t
         ql = q_lat.reshape(T * H, -1)
         qr = q_rot.reshape(T * H, -1)
         if split_tokens is None:
-            u, lse = finalize(*attend_absorbed(ql, qr, C, KR, cfg.softmax_scale, visible))
+            u, lse = finalize(*attend_absorbed(ql, qr, C, KR, scale, visible))
         else:
             n_split = -(-L // split_tokens)
-            parts = [attend_absorbed(ql, qr, C, KR, cfg.softmax_scale, visible, rg)
+            parts = [attend_absorbed(ql, qr, C, KR, scale, visible, rg)
                      for rg in split_ranges(L, split_tokens, n_split)]
             u, lse = combine_partials(parts)
         u = u.reshape(T, H, -1)

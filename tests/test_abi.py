@@ -151,3 +151,12 @@ def test_append_rejects_before_launch(B):
     a.ckv_dt = B.MLA_BF16
     a.c_in = fake + 8                                              # misaligned latent rows
     assert L.mla_cache_append(ctypes.byref(a), None) == 4
+
+
+def test_rope_freq_rejects_before_launch(B):
+    L = B.lib()
+    assert L.mla_rope_freq(None, None, 1, None, 4, 128, 63, None, None) == 4
+    assert L.mla_rope_freq(None, None, 2, None, 4, 128, 64, None, None) == 3
+    assert L.mla_rope_freq(None, None, 1, None, 4, 128, 64, None, None) == 1
+    assert L.mla_rope_freq(None, None, 1, None, 0, 128, 64, None, None) == 0    # empty: no-op
+    assert L.mla_rope_freq(None, None, 1, None, -1, 128, 64, None, None) == 2
