@@ -1,7 +1,8 @@
 """Benchmark of the MLA absorbed-decode hot path on one MI355X.
 
 One step = the whole path over one batch: mla_absorb_q -> mla_rope ->
-mla_decode_paged (split kernel + log-sum-exp combine) -> mla_out_proj, on the
+mla_decode_paged (split kernel, then the log-sum-exp combine fused with the
+per-head value up-projection W_UV), on the
 DeepSeek-V2-shaped layer B=32, H=128, S=4096, bf16 (synthetic, seeded; see
 mla_latent_kv_35_amd.synth). Inputs are resident in HBM before timing starts;
 the step cycles through enough replicas of the 151 MB paged cache that the
@@ -138,9 +139,10 @@ def main():
         c = caches[i % R]
         mla.absorb_q(d.q_nope, d.w_uk, out=q_lat)
         mla.rope(d.q_rope, d.positions, out=q_rot)
+        # the value up-projection runs inside the decode call (fused with the
+        # log-sum-exp combine when the plan splits the sequences)
         mla.decode_paged(q_lat, q_rot, c, cfg.T, cfg.softmax_scale, out=u, lse=lse,
-                         workspace=work)
-        mla.out_proj(u, d.w_uv, out=o)
+                         workspace=work, w_uv=d.w_uv, o=o)
 
     def decode_only(i):
         mla.decode_paged(q_lat, q_rot, caches[i % R], cfg.T, cfg.softmax_scale, out=u, lse=lse,

@@ -53,6 +53,8 @@ class DecodeArgs(ctypes.Structure):
         ("block_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
         ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("w_uv", ctypes.c_void_p), ("w_dt", ctypes.c_int32), ("o_dt", ctypes.c_int32),
+        ("o", ctypes.c_void_p),
     ]
 
 
@@ -277,8 +279,12 @@ def decode_plan(args: DecodeArgs):
 def decode_paged(q_lat: torch.Tensor, q_rope: torch.Tensor, cache: PagedCache, T: int,
                  softmax_scale: float, out: Optional[torch.Tensor] = None,
                  lse: Optional[torch.Tensor] = None, want_lse: bool = True, out_dtype=None,
-                 split_tokens: int = 0, workspace: Optional[torch.Tensor] = None, stream=None):
-    """u [B*T, H, 512] and lse [B*T, H] of absorbed MLA decode over the paged cache."""
+                 split_tokens: int = 0, workspace: Optional[torch.Tensor] = None, stream=None,
+                 w_uv: Optional[torch.Tensor] = None, o: Optional[torch.Tensor] = None):
+    """u [B*T, H, 512] and lse [B*T, H] of absorbed MLA decode over the paged cache.
+    With w_uv [H, 128, 512] the call also writes o [B*T, H, 128] = W_UV[h] u
+    (allocated when not given; fused with the combine when there are splits)
+    and returns (u, lse, o)."""
     a = make_decode_args(q_lat, q_rope, cache, T, softmax_scale, out, lse, out_dtype, split_tokens)
     BT, H, dc = q_lat.shape
     if out is None:
@@ -294,7 +300,13 @@ def decode_paged(q_lat: torch.Tensor, q_rope: torch.Tensor, cache: PagedCache, T
     a.out, a.lse = _ptr(out), _ptr(lse)
     a.workspace = _ptr(workspace) if ws else None
     a.workspace_bytes = workspace.numel() if ws else 0
+    if w_uv is not None:
+        if o is None:
+            o = torch.empty((BT, H, 128), dtype=out.dtype, device=q_lat.device)
+        a.w_uv, a.w_dt, a.o_dt, a.o = _ptr(w_uv), dtype_code(w_uv), dtype_code(o), _ptr(o)
     _check("mla_decode_paged", _lib.mla_decode_paged(ctypes.byref(a), _stream(stream)))
+    if w_uv is not None:
+        return out, lse, o
     return out, lse
 
 
@@ -350,13 +362,19 @@ def upload(inp, device="cuda") -> DeviceInputs:
         cache=cache, T=cfg.T, H=cfg.H, softmax_scale=cfg.softmax_scale)
 
 
-def decode_step(d: DeviceInputs, split_tokens: int = 0, stream=None, rope_base: float = 10000.0):
-    """One pass of the whole hot path: absorb -> rope -> paged decode (+combine) -> out-proj."""
+def decode_step(d: DeviceInputs, split_tokens: int = 0, stream=None, rope_base: float = 10000.0,
+                fused: bool = True):
+    """One pass of the whole hot path: absorb -> rope -> paged decode (+combine) -> out-proj.
+    fused: the projection runs inside mla_decode_paged (with the combine when
+    there are splits); otherwise as a separate mla_out_proj call."""
     q_lat = absorb_q(d.q_nope, d.w_uk, stream=stream)
     q_rot = rope(d.q_rope, d.positions, rope_base, stream=stream)
     u_dtype = torch.float32 if q_lat.dtype == torch.float32 else torch.bfloat16
-    u, lse = decode_paged(q_lat, q_rot, d.cache, d.T, d.softmax_scale, out_dtype=u_dtype,
-                          split_tokens=split_tokens, stream=stream)
-    o = out_proj(u, d.w_uv, out_dtype=torch.float32 if u_dtype == torch.float32 else torch.bfloat16,
-                 stream=stream)
+    if fused:
+        u, lse, o = decode_paged(q_lat, q_rot, d.cache, d.T, d.softmax_scale, out_dtype=u_dtype,
+                                 split_tokens=split_tokens, stream=stream, w_uv=d.w_uv)
+    else:
+        u, lse = decode_paged(q_lat, q_rot, d.cache, d.T, d.softmax_scale, out_dtype=u_dtype,
+                              split_tokens=split_tokens, stream=stream)
+        o = out_proj(u, d.w_uv, out_dtype=u_dtype, stream=stream)
     return dict(q_lat=q_lat, q_rot=q_rot, u=u, lse=lse, o=o)

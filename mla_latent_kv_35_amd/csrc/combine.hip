@@ -101,87 +101,204 @@ __device__ __forceinline__ float wave_sum64(float v) {
   return v;
 }
 
+// Merge of NR rows by one wave: lane i returns u for latent values 8i..8i+7
+// of each row (NaN for a sequence whose length or page count is out of
+// range) and each row's lse. The rows must be wave-uniform. Every load of
+// the first 8 splits (their (m, l) and U, from slots clamped to the
+// allocated n_split) is issued before the sequence length is known, so one
+// memory round trip serves all NR rows; splits past the live count are then
+// masked out and never accumulated.
+template <int NR>
+__device__ __forceinline__ void combine_rows(const CombineParams& p, const int (&row)[NR], int lane,
+                                             float (&u)[NR][8], float (&lse_out)[NR]) {
+  const int nsp = p.n_split;                                   // split stride in memory
+  const size_t kstride = (size_t)p.R * kDc;
+  int Ls[NR];
+  float mk[NR], lk[NR];
+  f32x4_t v0[NR][8], v1[NR][8];
+  const float* pu[NR];
+#pragma unroll
+  for (int t = 0; t < NR; ++t) {
+    const int b = row[t] / p.R, r = row[t] % p.R;
+    Ls[t] = p.seq_lens[b];
+    const float* ml = p.part_ml + (((size_t)b * nsp + min(lane, nsp - 1)) * p.R + r) * 2;
+    mk[t] = ml[0];
+    lk[t] = ml[1];
+    pu[t] = p.part_u + (((size_t)b * nsp) * p.R + r) * kDc + 8 * lane;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const size_t off = (size_t)min(q, nsp - 1) * kstride;
+      v0[t][q] = *(const f32x4_t*)(pu[t] + off);
+      v1[t][q] = *(const f32x4_t*)(pu[t] + off + 4);
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < NR; ++t) {
+    const int L = __builtin_amdgcn_readfirstlane(Ls[t]);
+    const bool bad = (L < p.T) || (L > p.max_seq_len) || ((L + kPage - 1) / kPage > p.max_pages);
+    if (bad) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) u[t][i] = __builtin_nanf("");
+      lse_out[t] = __builtin_nanf("");
+      continue;
+    }
+    const int ns = min(nsp, (L + p.split_tokens - 1) / p.split_tokens);
+    const float m_l = lane < ns ? mk[t] : -INFINITY;
+    const float l_l = lane < ns ? lk[t] : 0.f;
+    const float mx = wave_max64(m_l);
+    const float wk = (m_l == -INFINITY) ? 0.f : exp2f(m_l - mx);
+    const float lsum = wave_sum64(wk * l_l);
+    // split 0 is always live (L >= T >= 1); the split weights come from the
+    // lane that holds them (k is wave-uniform)
+    const float w0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk), 0));
+    f32x4_t acc0 = w0 * v0[t][0];
+    f32x4_t acc1 = w0 * v1[t][0];
+#pragma unroll
+    for (int q = 1; q < 8; ++q) {
+      if (q < ns) {
+        const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk), q));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc0[i] = fmaf(w, v0[t][q][i], acc0[i]);
+          acc1[i] = fmaf(w, v1[t][q][i], acc1[i]);
+        }
+      }
+    }
+    for (int k0 = 8; k0 < ns; k0 += 8) {
+      f32x4_t c0[8], c1[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const size_t off = (size_t)min(k0 + q, ns - 1) * kstride;
+        c0[q] = *(const f32x4_t*)(pu[t] + off);
+        c1[q] = *(const f32x4_t*)(pu[t] + off + 4);
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if (k0 + q < ns) {
+          const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk), k0 + q));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc0[i] = fmaf(w, c0[q][i], acc0[i]);
+            acc1[i] = fmaf(w, c1[q][i], acc1[i]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      u[t][i] = acc0[i] / lsum;
+      u[t][4 + i] = acc1[i] / lsum;
+    }
+    lse_out[t] = (mx + log2f(lsum)) * kLn2;
+  }
+}
+
+__device__ __forceinline__ void store_u_row(const CombineParams& p, int row, int lane,
+                                            const float (&u)[8], float lse) {
+  const size_t o = (size_t)row * kDc + 8 * lane;
+  if (p.out_bf16) {
+    u32x4_t ov;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ov[i] = pack_bf16x2(u[2 * i], u[2 * i + 1]);
+    *(u32x4_t*)((uint16_t*)p.out + o) = ov;
+  } else {
+    *(f32x4_t*)((float*)p.out + o) = (f32x4_t){u[0], u[1], u[2], u[3]};
+    *(f32x4_t*)((float*)p.out + o + 4) = (f32x4_t){u[4], u[5], u[6], u[7]};
+  }
+  if (p.lse && lane == 0) p.lse[row] = lse;
+}
+
 __global__ __launch_bounds__(64 * kWaveRows) void combine_wave_kernel(CombineParams p) {
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int row = __builtin_amdgcn_readfirstlane(blockIdx.x * kWaveRows + wv);  // b*R + r
   if (row >= p.rows) return;                      // the whole wave leaves; no barrier below
-  const int b = row / p.R, r = row % p.R;
-  const int L = __builtin_amdgcn_readfirstlane(p.seq_lens[b]);
-  const size_t o = (size_t)row * kDc + 8 * lane;
-  const bool bad = (L < p.T) || (L > p.max_seq_len) || ((L + kPage - 1) / kPage > p.max_pages);
-  if (bad) {
-    if (p.out_bf16) {
-      *(u32x4_t*)((uint16_t*)p.out + o) = (u32x4_t){0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u};
-    } else {
-      const float nan = __builtin_nanf("");
-      *(f32x4_t*)((float*)p.out + o) = (f32x4_t){nan, nan, nan, nan};
-      *(f32x4_t*)((float*)p.out + o + 4) = (f32x4_t){nan, nan, nan, nan};
-    }
-    if (p.lse && lane == 0) p.lse[row] = __builtin_nanf("");
-    return;
-  }
-  const int nsp = p.n_split;                                   // split stride in memory
-  const int ns = min(nsp, (L + p.split_tokens - 1) / p.split_tokens);
-  float mk = -INFINITY, lk = 0.f;
-  if (lane < ns) {
-    const float* ml = p.part_ml + (((size_t)b * nsp + lane) * p.R + r) * 2;
-    mk = ml[0];
-    lk = ml[1];
-  }
-  const float mx = wave_max64(mk);
-  const float wk = (mk == -INFINITY) ? 0.f : exp2f(mk - mx);
-  const float lsum = wave_sum64(wk * lk);
-  const float* pu = p.part_u + (((size_t)b * nsp) * p.R + r) * kDc + 8 * lane;
-  const size_t kstride = (size_t)p.R * kDc;
-  // split 0 is always live (L >= T >= 1)
-  // split weights come from the lane that holds them (k is wave-uniform)
-  const float w0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk), 0));
-  f32x4_t acc0 = w0 * *(const f32x4_t*)pu;
-  f32x4_t acc1 = w0 * *(const f32x4_t*)(pu + 4);
-  for (int k0 = 1; k0 < ns; k0 += 8) {
-    // loads of splits past the last live one repeat it (valid memory) and are
-    // not accumulated
-    f32x4_t v0[8], v1[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const size_t off = (size_t)min(k0 + q, ns - 1) * kstride;
-      v0[q] = *(const f32x4_t*)(pu + off);
-      v1[q] = *(const f32x4_t*)(pu + off + 4);
-    }
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      if (k0 + q < ns) {
-        const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk), k0 + q));
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc0[i] = fmaf(w, v0[q][i], acc0[i]);
-          acc1[i] = fmaf(w, v1[q][i], acc1[i]);
-        }
-      }
-    }
-  }
-  if (p.out_bf16) {
-    u32x4_t ov;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      ov[i] = pack_bf16x2(acc0[2 * i] / lsum, acc0[2 * i + 1] / lsum);
-      ov[i + 2] = pack_bf16x2(acc1[2 * i] / lsum, acc1[2 * i + 1] / lsum);
-    }
-    *(u32x4_t*)((uint16_t*)p.out + o) = ov;
+  const int rows[1] = {row};
+  float u[1][8], lse[1];
+  combine_rows<1>(p, rows, lane, u, lse);
+  store_u_row(p, row, lane, u[0], lse[0]);
+}
+
+// Combine fused with each head's value up-projection (V2 analysis page,
+// section 6.1: every head first aggregates its latents with its own weights,
+// then applies its own matrix, here W_UV[h]; the fused kernel the page
+// mentions as the alternative order of work). One workgroup of 8 waves per
+// (head h, 16 query tokens): each wave first issues its W_UV[h] fragments
+// (output dims 16w..16w+15, all 512 latent dims), then merges two of the
+// tokens' rows exactly as combine_wave_kernel does (one memory round trip
+// for both), writes u and lse, and stages u as bf16 in LDS; after one
+// barrier it computes its 16 x 16 block of o = u W_UV[h]^T on MFMA with the
+// same operands and k order as out_proj, so o equals combine followed by
+// out_proj bit for bit.
+constexpr int kOutTok = 16;
+constexpr int kOutThreads = 512;
+constexpr int kUPitch = kDc * 2 + 16;   // bf16 row + 16 B: rows start 4 banks apart
+
+__global__ __launch_bounds__(kOutThreads) void combine_out_kernel(CombineParams p, int n_rb) {
+  __shared__ __attribute__((aligned(16))) char ush_raw[kOutTok * kUPitch];
+  lds_char* const ush = (lds_char*)ush_raw;
+  // the row blocks of one head run on one XCD (they read the same W_UV[h])
+  int h, rb;
+  if (p.H % kNumXcd == 0) {
+    h = (blockIdx.x / (kNumXcd * n_rb)) * kNumXcd + blockIdx.x % kNumXcd;
+    rb = (blockIdx.x / kNumXcd) % n_rb;
   } else {
-    f32x4_t a, c;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      a[i] = acc0[i] / lsum;
-      c[i] = acc1[i] / lsum;
-    }
-    *(f32x4_t*)((float*)p.out + o) = a;
-    *(f32x4_t*)((float*)p.out + o + 4) = c;
+    h = blockIdx.x / n_rb;
+    rb = blockIdx.x % n_rb;
   }
-  if (p.lse && lane == 0) p.lse[row] = (mx + log2f(lsum)) * kLn2;
+  if (h >= p.H) return;                            // uniform over the workgroup
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int i16 = lane & 15, G4 = lane >> 4;
+  bf16x8_t wf[16];
+  const uint16_t* wrow = p.w_uv + ((size_t)h * kDh + 16 * wv + i16) * kDc + 8 * G4;
+#pragma unroll
+  for (int ks = 0; ks < 16; ++ks) wf[ks] = load_bf16x8(wrow + 32 * ks);
+  const int n0 = kOutTok * rb + 2 * wv;            // this wave's two tokens
+  u32x4_t packed[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+  if (n0 + 1 < p.n_tok) {                          // wave-uniform
+    const int rows[2] = {n0 * p.H + h, (n0 + 1) * p.H + h};
+    float u[2][8], lse[2];
+    combine_rows<2>(p, rows, lane, u, lse);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) packed[t][i] = pack_bf16x2(u[t][2 * i], u[t][2 * i + 1]);
+      if (p.out) store_u_row(p, rows[t], lane, u[t], lse[t]);
+    }
+  } else if (n0 < p.n_tok) {
+    const int rows[1] = {n0 * p.H + h};
+    float u[1][8], lse[1];
+    combine_rows<1>(p, rows, lane, u, lse);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) packed[0][i] = pack_bf16x2(u[0][2 * i], u[0][2 * i + 1]);
+    if (p.out) store_u_row(p, rows[0], lane, u[0], lse[0]);
+  }
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+    *(MLA_LDS u32x4_t*)(ush + (2 * wv + t) * kUPitch + lane * 16) = packed[t];
+  __syncthreads();
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < 16; ++ks)
+    acc = mfma16x16x32(lds_read_b128(ush + i16 * kUPitch + (4 * ks + G4) * 16), wf[ks], acc);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int n = kOutTok * rb + 4 * G4 + i;
+    if (n < p.n_tok) {
+      const size_t off = ((size_t)n * p.H + h) * kDh + 16 * wv + i16;
+      if (p.o_bf16) ((uint16_t*)p.o)[off] = f2bf(acc[i]);
+      else ((float*)p.o)[off] = acc[i];
+    }
+  }
 }
 
 }  // namespace
+
+hipError_t launch_combine_out(const CombineParams& p, hipStream_t s) {
+  if (p.n_split > 64 || !p.w_uv || !p.o) return hipErrorInvalidValue;
+  const int n_rb = (p.n_tok + kOutTok - 1) / kOutTok;
+  hipLaunchKernelGGL(combine_out_kernel, dim3(p.H * n_rb), dim3(kOutThreads), 0, s, p, n_rb);
+  return hipGetLastError();
+}
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t s) {
   if (p.n_split > kMaxSplitsLds) return hipErrorInvalidValue;

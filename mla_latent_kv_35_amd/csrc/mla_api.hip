@@ -187,6 +187,12 @@ int mla_decode_paged(const mla_decode_args* a, void* stream) {
   if (!a->q_lat || !a->q_rope || !a->ckv || !a->kr || !a->block_table || !a->seq_lens || !a->out)
     return MLA_ERR_NULL;
   if (a->ckv_dt == MLA_FP8_E4M3 && !a->ckv_scale) return MLA_ERR_NULL;
+  const bool proj = a->w_uv != nullptr;
+  if (proj) {
+    if (!a->o) return MLA_ERR_NULL;
+    if (!is_float_dt(a->w_dt) || !is_float_dt(a->o_dt)) return MLA_ERR_DTYPE;
+    if (a->w_dt == MLA_F32 && (a->out_dt != MLA_F32 || a->o_dt != MLA_F32)) return MLA_ERR_DTYPE;
+  }
   const Plan pl = make_plan(a);
   if (pl.n_split > 1) {
     if (!a->workspace || a->workspace_bytes < pl.ws_bytes) return MLA_ERR_WORKSPACE;
@@ -243,7 +249,21 @@ int mla_decode_paged(const mla_decode_args* a, void* stream) {
     c.max_seq_len = a->max_seq_len;
     c.max_pages = a->max_pages_per_seq;
     c.out_bf16 = p.out_bf16;
+    if (proj && a->w_dt == MLA_BF16 && pl.n_split <= 64) {
+      c.w_uv = (const uint16_t*)a->w_uv;
+      c.o = a->o;
+      c.o_bf16 = a->o_dt == MLA_BF16;
+      c.H = a->H;
+      c.n_tok = a->B * a->T;
+      e = launch_combine_out(c, s);
+      return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
+    }
     e = launch_combine(c, s);
+    if (e != hipSuccess) return MLA_ERR_LAUNCH;
+  }
+  if (proj) {
+    e = launch_out_proj(a->out, a->w_uv, a->o, p.out_bf16, a->w_dt == MLA_BF16,
+                        a->o_dt == MLA_BF16, a->B * a->T, a->H, s);
     if (e != hipSuccess) return MLA_ERR_LAUNCH;
   }
   return MLA_OK;

@@ -53,6 +53,11 @@ struct CombineParams {
   int R, T, n_split, split_tokens;
   int max_seq_len, max_pages;
   int out_bf16;
+  // fused value up-projection (combine_out): o[n][h] = W_UV[h] u[n][h]
+  const uint16_t* w_uv;     // [H][128][512] bf16, or null
+  void* o;                  // [n_tok][H][128]
+  int o_bf16;
+  int H, n_tok;             // n_tok = B*T
 };
 
 struct AppendParams {
@@ -79,6 +84,8 @@ hipError_t launch_decode_mfma_bf16(const DecodeParams& p, hipStream_t s);
 hipError_t launch_decode_mfma_fp8(const DecodeParams& p, hipStream_t s);
 hipError_t launch_decode_simple_f32(const DecodeParams& p, hipStream_t s);
 hipError_t launch_combine(const CombineParams& p, hipStream_t s);
+// combine fused with the value up-projection; needs p.w_uv, p.o, n_split <= 64
+hipError_t launch_combine_out(const CombineParams& p, hipStream_t s);
 
 // theta: device fp64 [d_r/2] per-pair frequencies, or null for base^(-2i/d_r)
 hipError_t launch_rope(const void* x_in, void* x_out, int bf16, const int32_t* pos, int n_tok,

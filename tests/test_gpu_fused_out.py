@@ -1,0 +1,70 @@
+"""The value up-projection inside mla_decode_paged (w_uv given): fused with
+the log-sum-exp combine when there are splits, a separate out-projection
+otherwise. The fused kernel merges rows exactly as the combine kernel does
+and multiplies with the same MFMA operands and k order as mla_out_proj, so
+u, lse and o must equal the unfused path (combine, then mla_out_proj) bit
+for bit; the whole-step parity tests compare o with the oracle."""
+import numpy as np
+import pytest
+import torch
+
+from mla_latent_kv_35_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def bits(t):
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy()
+    return t.cpu().numpy().view(np.int32)
+
+
+CASES = [
+    dict(B=3, H=128, T=1, seq_len=700, ragged=True, permuted=True, split=128),
+    dict(B=5, H=32, T=2, seq_len=333, ragged=True, permuted=True, split=64),      # 10 tokens
+    dict(B=1, H=16, T=1, seq_len=900, ragged=False, split=64),                    # 1 token, 15 splits
+    dict(B=17, H=64, T=1, seq_len=200, ragged=True, split=64),                    # 17 tokens: 2 blocks
+    dict(B=4, H=128, T=2, seq_len=300, ragged=False, ckv_dt="fp8", split=128),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"B{c['B']}H{c['H']}T{c['T']}s{c['split']}")
+def test_fused_equals_unfused_bit_exact(mla, case):
+    case = dict(case)
+    split = case.pop("split")
+    ckv_dt = case.pop("ckv_dt", "bf16")
+    cfg = synth.small_config("fused", ckv_dt=ckv_dt, seed=61 + case["B"], **case)
+    inp = synth.make_inputs(cfg)
+    d = mla.upload(inp)
+    fused = mla.decode_step(d, split_tokens=split, fused=True)
+    plain = mla.decode_step(d, split_tokens=split, fused=False)
+    torch.cuda.synchronize()
+    for k in ("u", "lse", "o"):
+        assert np.array_equal(bits(fused[k]), bits(plain[k])), k
+    assert not torch.isnan(fused["o"]).any()
+
+
+def test_fused_projection_f32_output_and_no_split(mla):
+    cfg = synth.small_config("fused_f32o", B=6, H=32, T=1, seq_len=400, ragged=True, seed=71)
+    inp = synth.make_inputs(cfg)
+    d = mla.upload(inp)
+    q_lat = mla.absorb_q(d.q_nope, d.w_uk)
+    q_rot = mla.rope(d.q_rope, d.positions)
+    for split in (64, 448):                    # several splits (fused), then one (separate launch)
+        o32 = torch.empty((6, 32, 128), dtype=torch.float32, device="cuda")
+        u, lse, o = mla.decode_paged(q_lat, q_rot, d.cache, 1, cfg.softmax_scale,
+                                     split_tokens=split, w_uv=d.w_uv, o=o32)
+        ref = mla.out_proj(u, d.w_uv, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(o), bits(ref)), split
+
+
+def test_fused_projection_of_bad_sequence_is_nan(mla):
+    cfg = synth.small_config("fused_bad", B=3, H=16, T=1, seq_len=300, ragged=False, seed=72)
+    inp = synth.make_inputs(cfg)
+    d = mla.upload(inp)
+    d.cache.seq_lens[1] = d.cache.max_seq_len + 5
+    out = mla.decode_step(d, split_tokens=64, fused=True)
+    torch.cuda.synchronize()
+    o = out["o"].float().cpu().numpy()
+    assert np.isnan(o[1]).all() and not np.isnan(o[[0, 2]]).any()
