@@ -281,6 +281,43 @@ typedef struct mla_append_args {
  */
 int mla_cache_append(const mla_append_args* args, void* stream);
 
+/*
+ * mla_expand_kv -- the expanded keys and values of prefill (V2 analysis
+ * page, section 6.1: training and long-prompt prefill expand the latents per
+ * head and run ordinary attention; the expansion lives only inside the
+ * current block):
+ *   k_nope[n][h][:] = W_UK[h] c[n],  v[n][h][:] = W_UV[h] c[n]
+ *   c            : [n_tok][d_c]     dtype c_dt (F32 or BF16), the latents
+ *   w_uk, w_uv   : [H][d_h][d_c]    dtype w_dt (BF16, or F32 with F32 c and outputs)
+ *   k_nope, v    : [n_tok][H][d_h]  dtype out_dt (F32 or BF16)
+ * Supported: d_h = 128, d_c = 512; fp32 accumulation (as mla_out_proj).
+ */
+int mla_expand_kv(const void* c, const void* w_uk, const void* w_uv, void* k_nope, void* v,
+                  int c_dt, int w_dt, int out_dt, int n_tok, int H, int d_h, int d_c,
+                  void* stream);
+
+/*
+ * mla_prefill_attn -- causal attention on expanded keys (V2 analysis page,
+ * section 6.1; the same function as the absorbed decode in exact
+ * arithmetic). Head h's key for token s is [k_nope[s][h] ; k_rope[s]]
+ * (d_h + d_r = 192 values; the rope key is shared by the heads, section 1.3),
+ * its value v[s][h] (128 values). Query i of sequence b sits at position
+ * n_kv - n_q + i (the queries are the last n_q tokens) and attends to keys
+ * s <= n_kv - n_q + i:
+ *   o[b][i][h] = sum_s softmax_s(scale * (q_nope.k_nope_s + q_rope.k_rope_s)) v_s
+ *   q_nope : [B][n_q][H][d_h]  BF16      q_rope : [B][n_q][H][d_r] BF16 (rotated)
+ *   k_nope : [B][n_kv][H][d_h] BF16      k_rope : [B][n_kv][d_r]   BF16 (rotated)
+ *   v      : [B][n_kv][H][d_h] BF16
+ *   o      : [B][n_q][H][d_h]  dtype o_dt (F32 or BF16)
+ *   lse    : [B][n_q][H] fp32 natural-log sum of exp(scores), or NULL
+ * Supported: d_h = 128, d_r = 64, 1 <= n_q <= n_kv, 16-byte aligned tensors.
+ * bf16 MFMA, fp32 softmax and accumulation.
+ */
+int mla_prefill_attn(const void* q_nope, const void* q_rope, const void* k_nope,
+                     const void* k_rope, const void* v, void* o, float* lse, int o_dt, int B,
+                     int n_q, int n_kv, int H, int d_h, int d_r, float softmax_scale,
+                     void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -93,6 +93,11 @@ _lib.mla_yarn_frequencies.restype = _i
 _lib.mla_yarn_frequencies.argtypes = [_i, _d, _d, _d, _d, _i, ctypes.POINTER(_d)]
 _lib.mla_yarn_mscale.restype = _d
 _lib.mla_yarn_mscale.argtypes = [_d, _d]
+_lib.mla_expand_kv.restype = _i
+_lib.mla_expand_kv.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]
+_lib.mla_prefill_attn.restype = _i
+_lib.mla_prefill_attn.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i,
+                                  ctypes.c_float, _vp]
 _lib.mla_cache_append.restype = _i
 _lib.mla_cache_append.argtypes = [ctypes.POINTER(AppendArgs), _vp]
 _lib.mla_out_proj.restype = _i
@@ -100,7 +105,8 @@ _lib.mla_out_proj.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]
 
 EXPORTED = ["mla_status_str", "mla_abi_version", "mla_absorb_q", "mla_rope",
             "mla_decode_plan", "mla_decode_paged", "mla_out_proj", "mla_cache_append",
-            "mla_rope_freq", "mla_yarn_frequencies", "mla_yarn_mscale"]
+            "mla_rope_freq", "mla_yarn_frequencies", "mla_yarn_mscale", "mla_expand_kv",
+            "mla_prefill_attn"]
 
 
 def lib():
@@ -177,6 +183,37 @@ def rope_freq(x: torch.Tensor, pos: torch.Tensor, theta: torch.Tensor,
     _check("mla_rope_freq", _lib.mla_rope_freq(_ptr(x), _ptr(out), dtype_code(x), _ptr(pos), n,
                                                heads, dr, _ptr(theta), _stream(stream)))
     return out
+
+
+def expand_kv(c: torch.Tensor, w_uk: torch.Tensor, w_uv: torch.Tensor, out_dtype=None,
+              stream=None):
+    """Per-head keys W_UK[h] c and values W_UV[h] c of latents c [n, 512]:
+    (k_nope [n, H, 128], v [n, H, 128])."""
+    n = c.shape[0]
+    H, dh, dc = w_uk.shape
+    dt = out_dtype or (torch.float32 if c.dtype == torch.float32 else torch.bfloat16)
+    k = torch.empty((n, H, dh), dtype=dt, device=c.device)
+    v = torch.empty_like(k)
+    _check("mla_expand_kv", _lib.mla_expand_kv(_ptr(c), _ptr(w_uk), _ptr(w_uv), _ptr(k), _ptr(v),
+                                               dtype_code(c), dtype_code(w_uk), dtype_code(k),
+                                               n, H, dh, dc, _stream(stream)))
+    return k, v
+
+
+def prefill_attn(q_nope: torch.Tensor, q_rope: torch.Tensor, k_nope: torch.Tensor,
+                 k_rope: torch.Tensor, v: torch.Tensor, softmax_scale: float, out_dtype=None,
+                 want_lse: bool = True, stream=None):
+    """Causal attention on expanded keys: q_nope [B, n_q, H, 128], q_rope
+    [B, n_q, H, 64], k_nope / v [B, n_kv, H, 128], k_rope [B, n_kv, 64] ->
+    (o [B, n_q, H, 128], lse [B, n_q, H])."""
+    B, n_q, H, dh = q_nope.shape
+    n_kv, dr = k_nope.shape[1], q_rope.shape[3]
+    o = torch.empty((B, n_q, H, dh), dtype=out_dtype or q_nope.dtype, device=q_nope.device)
+    lse = torch.empty((B, n_q, H), dtype=torch.float32, device=q_nope.device) if want_lse else None
+    _check("mla_prefill_attn", _lib.mla_prefill_attn(
+        _ptr(q_nope), _ptr(q_rope), _ptr(k_nope), _ptr(k_rope), _ptr(v), _ptr(o), _ptr(lse),
+        dtype_code(o), B, n_q, n_kv, H, dh, dr, softmax_scale, _stream(stream)))
+    return o, lse
 
 
 def yarn_frequencies(d_r: int = 64, base: float = 10000.0, factor: float = 40.0,

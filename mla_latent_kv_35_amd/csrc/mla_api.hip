@@ -282,6 +282,56 @@ int mla_out_proj(const void* u, const void* w_uv, void* o, int u_dt, int w_dt, i
   return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
 }
 
+int mla_expand_kv(const void* c, const void* w_uk, const void* w_uv, void* k_nope, void* v,
+                  int c_dt, int w_dt, int out_dt, int n_tok, int H, int d_h, int d_c,
+                  void* stream) {
+  if (n_tok < 0 || H < 1) return MLA_ERR_SHAPE;
+  if (d_h != kDh || d_c != kDc) return MLA_ERR_UNSUPPORTED;
+  if (!is_float_dt(c_dt) || !is_float_dt(w_dt) || !is_float_dt(out_dt)) return MLA_ERR_DTYPE;
+  if (w_dt == MLA_F32 && (c_dt != MLA_F32 || out_dt != MLA_F32)) return MLA_ERR_DTYPE;
+  if (n_tok == 0) return MLA_OK;
+  if (!c || !w_uk || !w_uv || !k_nope || !v) return MLA_ERR_NULL;
+  const hipStream_t s = (hipStream_t)stream;
+  for (int i = 0; i < 2; ++i) {
+    const hipError_t e = launch_out_proj_strided(c, kDc, 0, i == 0 ? w_uk : w_uv,
+                                                 i == 0 ? k_nope : v, c_dt == MLA_BF16,
+                                                 w_dt == MLA_BF16, out_dt == MLA_BF16, n_tok, H, s);
+    if (e != hipSuccess) return MLA_ERR_LAUNCH;
+  }
+  return MLA_OK;
+}
+
+int mla_prefill_attn(const void* q_nope, const void* q_rope, const void* k_nope,
+                     const void* k_rope, const void* v, void* o, float* lse, int o_dt, int B,
+                     int n_q, int n_kv, int H, int d_h, int d_r, float softmax_scale,
+                     void* stream) {
+  if (B < 1 || H < 1 || n_q < 1 || n_kv < n_q) return MLA_ERR_SHAPE;
+  if (d_h != kDh || d_r != kDr) return MLA_ERR_UNSUPPORTED;
+  if (!is_float_dt(o_dt)) return MLA_ERR_DTYPE;
+  if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return MLA_ERR_SHAPE;
+  if ((int64_t)B * H * ((n_q + 63) / 64) > INT32_MAX) return MLA_ERR_UNSUPPORTED;
+  if (!q_nope || !q_rope || !k_nope || !k_rope || !v || !o) return MLA_ERR_NULL;
+  const uintptr_t al = (uintptr_t)q_nope | (uintptr_t)q_rope | (uintptr_t)k_nope |
+                       (uintptr_t)k_rope | (uintptr_t)v | (uintptr_t)o;
+  if (al % 16 != 0) return MLA_ERR_UNSUPPORTED;
+  PrefillParams p{};
+  p.q_nope = q_nope;
+  p.q_rope = q_rope;
+  p.k_nope = k_nope;
+  p.k_rope = k_rope;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.B = B;
+  p.n_q = n_q;
+  p.n_kv = n_kv;
+  p.H = H;
+  p.o_bf16 = o_dt == MLA_BF16;
+  p.scale_log2 = softmax_scale * kLog2e;
+  const hipError_t e = launch_prefill(p, (hipStream_t)stream);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
+}
+
 int mla_cache_append(const mla_append_args* a, void* stream) {
   if (!a) return MLA_ERR_NULL;
   if (a->n_tok < 0 || a->B < 1 || a->n_pages < 1 || a->max_pages_per_seq < 1 || a->reserved0 != 0)

@@ -80,6 +80,21 @@ struct AppendParams {
 };
 
 hipError_t launch_append(const AppendParams& p, hipStream_t s);
+
+struct PrefillParams {
+  const void* q_nope;       // [B][n_q][H][128] bf16
+  const void* q_rope;       // [B][n_q][H][64] bf16, rotated
+  const void* k_nope;       // [B][n_kv][H][128] bf16 (W_UK[h] c)
+  const void* k_rope;       // [B][n_kv][64] bf16, rotated, shared by the heads
+  const void* v;            // [B][n_kv][H][128] bf16 (W_UV[h] c)
+  void* o;                  // [B][n_q][H][128]
+  float* lse;               // [B][n_q][H] or null
+  int B, n_q, n_kv, H;
+  int o_bf16;
+  float scale_log2;
+};
+
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t s);
 hipError_t launch_decode_mfma_bf16(const DecodeParams& p, hipStream_t s);
 hipError_t launch_decode_mfma_fp8(const DecodeParams& p, hipStream_t s);
 hipError_t launch_decode_simple_f32(const DecodeParams& p, hipStream_t s);
@@ -92,6 +107,10 @@ hipError_t launch_rope(const void* x_in, void* x_out, int bf16, const int32_t* p
                        int n_heads, int d_r, double base, const double* theta, hipStream_t s);
 hipError_t launch_absorb(const void* q_nope, const void* w_uk, void* q_lat, int in_bf16,
                          int out_bf16, int n_tok, int H, hipStream_t s);
+// o[n][h][:] = W[h] u(n, h), u(n, h) at n * u_tok + h * u_head elements
+hipError_t launch_out_proj_strided(const void* u, long u_tok, long u_head, const void* w_uv,
+                                   void* o, int u_bf16, int w_bf16, int o_bf16, int n_tok, int H,
+                                   hipStream_t s);
 hipError_t launch_out_proj(const void* u, const void* w_uv, void* o, int u_bf16, int w_bf16,
                            int o_bf16, int n_tok, int H, hipStream_t s);
 

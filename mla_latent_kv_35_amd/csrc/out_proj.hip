@@ -33,11 +33,15 @@ __device__ __forceinline__ bf16x8_t load_row8(const void* base, size_t off, bool
 // head, which read the same u rows, share an XCD (and its L2).
 constexpr int kTokTile = 32;
 
+// u row of (token n, head h) starts at n * u_tok + h * u_head elements:
+// (H * 512, 512) for per-head aggregates; (512, 0) for a latent shared by
+// every head (the key / value expansion of prefill).
 template <bool U_BF16, bool O_BF16>
 __global__ __launch_bounds__(kThreads) void out_proj_bf16_kernel(const void* __restrict__ u,
                                                                  const uint16_t* __restrict__ wuv,
                                                                  void* __restrict__ o, int n_tok,
-                                                                 int H, int n_tb) {
+                                                                 int H, int n_tb, long u_tok,
+                                                                 long u_head) {
   // blocks on XCD x (= blockIdx % 8) serve the heads h with h % 8 == x
   const int x = blockIdx.x % kNumXcd, idx = blockIdx.x / kNumXcd;
   const int per_head = 2 * n_tb;
@@ -60,7 +64,8 @@ __global__ __launch_bounds__(kThreads) void out_proj_bf16_kernel(const void* __r
 #pragma unroll
     for (int ks = 0; ks < 16; ++ks) {
       a[tt][ks] = (bf16x8_t){0, 0, 0, 0, 0, 0, 0, 0};
-      if (na < n_tok) a[tt][ks] = load_row8(u, ((size_t)na * H + h) * kDc + 32 * ks + 8 * G4, U_BF16);
+      if (na < n_tok)
+        a[tt][ks] = load_row8(u, (size_t)na * u_tok + (size_t)h * u_head + 32 * ks + 8 * G4, U_BF16);
     }
   }
   f32x4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
@@ -83,11 +88,13 @@ __global__ __launch_bounds__(kThreads) void out_proj_bf16_kernel(const void* __r
 
 __global__ __launch_bounds__(kDh) void out_proj_f32_kernel(const float* __restrict__ u,
                                                           const float* __restrict__ wuv,
-                                                          float* __restrict__ o, int H) {
+                                                          float* __restrict__ o, int H, long u_tok,
+                                                          long u_head) {
   __shared__ float us[kDc];
   const int nh = blockIdx.x;
   const int h = nh % H;
-  for (int d = threadIdx.x; d < kDc; d += kDh) us[d] = u[(size_t)nh * kDc + d];
+  const float* ur = u + (size_t)(nh / H) * u_tok + (size_t)h * u_head;
+  for (int d = threadIdx.x; d < kDc; d += kDh) us[d] = ur[d];
   __syncthreads();
   const int j = threadIdx.x;
   const float* wr = wuv + ((size_t)h * kDh + j) * kDc;
@@ -100,22 +107,33 @@ __global__ __launch_bounds__(kDh) void out_proj_f32_kernel(const float* __restri
 
 hipError_t launch_out_proj(const void* u, const void* w_uv, void* o, int u_bf16, int w_bf16,
                            int o_bf16, int n_tok, int H, hipStream_t s) {
+  return launch_out_proj_strided(u, (long)H * kDc, kDc, w_uv, o, u_bf16, w_bf16, o_bf16, n_tok, H,
+                                 s);
+}
+
+hipError_t launch_out_proj_strided(const void* u, long u_tok, long u_head, const void* w_uv,
+                                   void* o, int u_bf16, int w_bf16, int o_bf16, int n_tok, int H,
+                                   hipStream_t s) {
   if (n_tok == 0) return hipSuccess;
   if (w_bf16) {
     const int n_tb = (n_tok + kTokTile - 1) / kTokTile;
     const dim3 grid(kNumXcd * ((H + kNumXcd - 1) / kNumXcd) * 2 * n_tb);
     const uint16_t* w = (const uint16_t*)w_uv;
     if (u_bf16 && o_bf16)
-      hipLaunchKernelGGL((out_proj_bf16_kernel<true, true>), grid, dim3(kThreads), 0, s, u, w, o, n_tok, H, n_tb);
+      hipLaunchKernelGGL((out_proj_bf16_kernel<true, true>), grid, dim3(kThreads), 0, s, u, w, o, n_tok, H, n_tb,
+                         u_tok, u_head);
     else if (u_bf16)
-      hipLaunchKernelGGL((out_proj_bf16_kernel<true, false>), grid, dim3(kThreads), 0, s, u, w, o, n_tok, H, n_tb);
+      hipLaunchKernelGGL((out_proj_bf16_kernel<true, false>), grid, dim3(kThreads), 0, s, u, w, o, n_tok, H, n_tb,
+                         u_tok, u_head);
     else if (o_bf16)
-      hipLaunchKernelGGL((out_proj_bf16_kernel<false, true>), grid, dim3(kThreads), 0, s, u, w, o, n_tok, H, n_tb);
+      hipLaunchKernelGGL((out_proj_bf16_kernel<false, true>), grid, dim3(kThreads), 0, s, u, w, o, n_tok, H, n_tb,
+                         u_tok, u_head);
     else
-      hipLaunchKernelGGL((out_proj_bf16_kernel<false, false>), grid, dim3(kThreads), 0, s, u, w, o, n_tok, H, n_tb);
+      hipLaunchKernelGGL((out_proj_bf16_kernel<false, false>), grid, dim3(kThreads), 0, s, u, w, o, n_tok, H, n_tb,
+                         u_tok, u_head);
   } else {
     hipLaunchKernelGGL(out_proj_f32_kernel, dim3(n_tok * H), dim3(kDh), 0, s, (const float*)u,
-                       (const float*)w_uv, (float*)o, H);
+                       (const float*)w_uv, (float*)o, H, u_tok, u_head);
   }
   return hipGetLastError();
 }
