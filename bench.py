@@ -220,6 +220,42 @@ def main():
     torch.cuda.synchronize()
     dur_ms["append"] = a0.elapsed_time(a1) / (n_dec * per_graph)
 
+    # prefill in the explicit form, one sequence of this workload's length
+    # (at most 4096) and all heads: key/value expansion, then causal attention
+    prefill = None
+    if cfg.q_dt == "bf16":
+        n = min(cfg.seq_len, 4096)
+        gen = torch.Generator(device="cuda").manual_seed(11)
+        c_p = torch.randn((n, 512), device="cuda", generator=gen).to(torch.bfloat16)
+        kr_p = torch.randn((1, n, 64), device="cuda", generator=gen).to(torch.bfloat16)
+        qn_p = torch.randn((1, n, H, 128), device="cuda", generator=gen).to(torch.bfloat16)
+        qr_p = torch.randn((1, n, H, 64), device="cuda", generator=gen).to(torch.bfloat16)
+        k_p, v_p = mla.expand_kv(c_p, d.w_uk, d.w_uv)
+        k_p, v_p = k_p.view(1, n, H, 128), v_p.view(1, n, H, 128)
+        o_p = torch.empty((1, n, H, 128), dtype=torch.bfloat16, device="cuda")
+
+        def timed(fn, reps=5):
+            g = capture(lambda i: fn(), reps)
+            g.replay()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(4):
+                g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / (4 * reps)
+
+        attn_ms = timed(lambda: mla.prefill_attn(qn_p, qr_p, k_p, kr_p, v_p, cfg.softmax_scale,
+                                                 want_lse=False, out=o_p))
+        exp_ms = timed(lambda: mla.expand_kv(c_p, d.w_uk, d.w_uv))
+        pf_flops = H * (n * (n + 1) / 2) * 2 * (192 + 128)
+        prefill = {"workload": f"one sequence, n_q = n_kv = {n}, H = {H}, causal, bf16",
+                   "attn_ms": round(attn_ms, 4),
+                   "attn_tflops": round(pf_flops / (attn_ms * 1e-3) / 1e12, 1),
+                   "mfma_frac_bf16": round(pf_flops / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                   "expand_ms": round(exp_ms, 4)}
+
     tokens = cfg.B * cfg.T
     value = tokens * steps / el
     dec_s = dur_ms["decode"] * 1e-3
@@ -247,6 +283,7 @@ def main():
         "decode_ms": round(dur_ms["decode"], 5),
         "eager_ms_per_step": round(el_eager / steps * 1e3, 5),
         "append_ms": round(dur_ms["append"], 5),
+        "prefill": prefill,
         "launch": "hip graph of %d steps per replay" % per_graph,
         "roofline": {
             "kernel": "mla_decode_paged (split-KV kernel + log-sum-exp combine)",

@@ -202,13 +202,14 @@ def expand_kv(c: torch.Tensor, w_uk: torch.Tensor, w_uv: torch.Tensor, out_dtype
 
 def prefill_attn(q_nope: torch.Tensor, q_rope: torch.Tensor, k_nope: torch.Tensor,
                  k_rope: torch.Tensor, v: torch.Tensor, softmax_scale: float, out_dtype=None,
-                 want_lse: bool = True, stream=None):
+                 want_lse: bool = True, out: Optional[torch.Tensor] = None, stream=None):
     """Causal attention on expanded keys: q_nope [B, n_q, H, 128], q_rope
     [B, n_q, H, 64], k_nope / v [B, n_kv, H, 128], k_rope [B, n_kv, 64] ->
     (o [B, n_q, H, 128], lse [B, n_q, H])."""
     B, n_q, H, dh = q_nope.shape
     n_kv, dr = k_nope.shape[1], q_rope.shape[3]
-    o = torch.empty((B, n_q, H, dh), dtype=out_dtype or q_nope.dtype, device=q_nope.device)
+    o = out if out is not None else torch.empty((B, n_q, H, dh), dtype=out_dtype or q_nope.dtype,
+                                                device=q_nope.device)
     lse = torch.empty((B, n_q, H), dtype=torch.float32, device=q_nope.device) if want_lse else None
     _check("mla_prefill_attn", _lib.mla_prefill_attn(
         _ptr(q_nope), _ptr(q_rope), _ptr(k_nope), _ptr(k_rope), _ptr(v), _ptr(o), _ptr(lse),

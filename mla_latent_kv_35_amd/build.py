@@ -19,7 +19,8 @@ LIB = os.path.join(PKG, "libmla.so")
 ARCH = "gfx950"
 
 SOURCES = ["mla_api.hip", "decode_mfma.hip", "decode_simple.hip", "combine.hip",
-           "rope.hip", "absorb.hip", "out_proj.hip", "append.hip", "prefill.hip"]
+           "rope.hip", "absorb.hip", "out_proj.hip", "append.hip", "prefill.hip",
+           "gemm_nt.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

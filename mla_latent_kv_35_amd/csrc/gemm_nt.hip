@@ -1,0 +1,121 @@
+// C[m][n] = sum_k A[m][k] B[n][k] on bf16 MFMA with fp32 accumulation: the
+// key / value expansion of prefill (PaperTrace "02 · DeepSeek-V2 analysis",
+// section 6.1), where A = the latents [n_tok][512] and B = the per-head
+// up-projections flattened to [H*128][512], so C[n][h*128 + j] = W[h] c[n].
+//
+// One workgroup of 4 waves per 128 x 128 tile of C; wave (wm, wn) owns the
+// 64 x 64 quarter (4 x 4 MFMA 16x16x32 blocks). K streams through LDS in
+// chunks of 32 (one MFMA k-step), double-buffered: the next chunk's global
+// loads are in flight while the current one is multiplied. LDS rows are
+// 80 B apart (64 B of data + 16 B), so the 16 rows of an operand fragment
+// start on 16 different bank quadruples.
+#include "mla_device.h"
+#include "mla_internal.h"
+
+namespace mla {
+namespace {
+
+constexpr int kTile = 128;
+constexpr int kKc = 32;
+constexpr int kPitch = 80;                         // bytes per LDS row
+constexpr int kBuf = kTile * kPitch;               // one operand chunk: 10 KB
+
+template <bool A_BF16, bool C_BF16>
+__global__ __launch_bounds__(256) void gemm_nt_kernel(const void* __restrict__ A,
+                                                      const uint16_t* __restrict__ Bm,
+                                                      void* __restrict__ C, int M, int N, int K) {
+  __shared__ __attribute__((aligned(16))) char smem_raw[4 * kBuf];   // A[2], B[2]
+  lds_char* const smem = (lds_char*)smem_raw;
+  const int m0 = blockIdx.y * kTile, n0 = blockIdx.x * kTile;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int i16 = lane & 15, G4 = lane >> 4;
+  const int wm = w >> 1, wn = w & 1;
+  // loads: a chunk of A (or B) is 128 rows x 64 B = 512 pieces of 16 B; 2 per thread
+  u32x4_t ra[2], rb[2];
+  auto load = [&](int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int e = tid + 256 * i, r = e >> 2, c = e & 3;
+      const int m = m0 + r;
+      ra[i] = (u32x4_t){0u, 0u, 0u, 0u};
+      if (m < M) {
+        if constexpr (A_BF16) {
+          ra[i] = *(const u32x4_t*)((const uint16_t*)A + (size_t)m * K + k0 + 8 * c);
+        } else {
+          const float* src = (const float*)A + (size_t)m * K + k0 + 8 * c;
+          const f32x4_t lo = *(const f32x4_t*)src, hi = *(const f32x4_t*)(src + 4);
+          ra[i] = (u32x4_t){pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]),
+                            pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3])};
+        }
+      }
+      rb[i] = *(const u32x4_t*)(Bm + (size_t)(n0 + r) * K + k0 + 8 * c);   // N % 128 == 0
+    }
+  };
+  auto store = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int e = tid + 256 * i, r = e >> 2, c = e & 3;
+      *(MLA_LDS u32x4_t*)(smem + buf * kBuf + r * kPitch + 16 * c) = ra[i];
+      *(MLA_LDS u32x4_t*)(smem + (2 + buf) * kBuf + r * kPitch + 16 * c) = rb[i];
+    }
+  };
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  const int nk = K / kKc;
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int kc = 0; kc < nk; ++kc) {
+    const int cur = kc & 1;
+    if (kc + 1 < nk) load((kc + 1) * kKc);
+    bf16x8_t a[4], b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[i] = lds_read_b128(smem + cur * kBuf + (64 * wm + 16 * i + i16) * kPitch + 16 * G4);
+      b[i] = lds_read_b128(smem + (2 + cur) * kBuf + (64 * wn + 16 * i + i16) * kPitch + 16 * G4);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(a[i], b[j], acc[i][j]);
+    if (kc + 1 < nk) store(cur ^ 1);            // the other buffer was last read one chunk ago
+    __syncthreads();
+  }
+  // lane holds C[64wm + 16i + 4*G4 + r][64wn + 16j + i16]
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = m0 + 64 * wm + 16 * i + 4 * G4 + r;
+      if (m >= M) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const size_t off = (size_t)m * N + n0 + 64 * wn + 16 * j + i16;
+        if (C_BF16) ((uint16_t*)C)[off] = f2bf(acc[i][j][r]);
+        else ((float*)C)[off] = acc[i][j][r];
+      }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_nt(const void* A, int a_bf16, const uint16_t* B, void* C, int c_bf16, int M,
+                          int N, int K, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  if (N % kTile != 0 || K % kKc != 0) return hipErrorInvalidValue;
+  const dim3 grid(N / kTile, (M + kTile - 1) / kTile);
+  if (a_bf16 && c_bf16)
+    hipLaunchKernelGGL((gemm_nt_kernel<true, true>), grid, dim3(256), 0, s, A, B, C, M, N, K);
+  else if (a_bf16)
+    hipLaunchKernelGGL((gemm_nt_kernel<true, false>), grid, dim3(256), 0, s, A, B, C, M, N, K);
+  else if (c_bf16)
+    hipLaunchKernelGGL((gemm_nt_kernel<false, true>), grid, dim3(256), 0, s, A, B, C, M, N, K);
+  else
+    hipLaunchKernelGGL((gemm_nt_kernel<false, false>), grid, dim3(256), 0, s, A, B, C, M, N, K);
+  return hipGetLastError();
+}
+
+}  // namespace mla

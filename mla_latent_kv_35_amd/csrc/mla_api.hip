@@ -293,9 +293,14 @@ int mla_expand_kv(const void* c, const void* w_uk, const void* w_uv, void* k_nop
   if (!c || !w_uk || !w_uv || !k_nope || !v) return MLA_ERR_NULL;
   const hipStream_t s = (hipStream_t)stream;
   for (int i = 0; i < 2; ++i) {
-    const hipError_t e = launch_out_proj_strided(c, kDc, 0, i == 0 ? w_uk : w_uv,
-                                                 i == 0 ? k_nope : v, c_dt == MLA_BF16,
-                                                 w_dt == MLA_BF16, out_dt == MLA_BF16, n_tok, H, s);
+    const void* w = i == 0 ? w_uk : w_uv;
+    void* out = i == 0 ? k_nope : v;
+    // bf16 weights: one GEMM over all heads, [n_tok][512] x [H*128][512]^T
+    const hipError_t e =
+        w_dt == MLA_BF16
+            ? launch_gemm_nt(c, c_dt == MLA_BF16, (const uint16_t*)w, out, out_dt == MLA_BF16,
+                             n_tok, H * kDh, kDc, s)
+            : launch_out_proj_strided(c, kDc, 0, w, out, 0, 0, 0, n_tok, H, s);
     if (e != hipSuccess) return MLA_ERR_LAUNCH;
   }
   return MLA_OK;

@@ -95,6 +95,9 @@ struct PrefillParams {
 };
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t s);
+// C[M][N] = A[M][K] B[N][K]^T, B bf16, A f32 or bf16; N % 128 == 0, K % 32 == 0
+hipError_t launch_gemm_nt(const void* A, int a_bf16, const uint16_t* B, void* C, int c_bf16, int M,
+                          int N, int K, hipStream_t s);
 hipError_t launch_decode_mfma_bf16(const DecodeParams& p, hipStream_t s);
 hipError_t launch_decode_mfma_fp8(const DecodeParams& p, hipStream_t s);
 hipError_t launch_decode_simple_f32(const DecodeParams& p, hipStream_t s);
