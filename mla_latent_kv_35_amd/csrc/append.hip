@@ -11,7 +11,7 @@
 // with one vector store. Lanes 0-31 rotate rope pair i = lane in fp64, as the
 // rope kernel does.
 #include "mla_device.h"
-#include "mla_internal.h"
+#include "mla_extra.h"
 
 namespace mla {
 namespace {

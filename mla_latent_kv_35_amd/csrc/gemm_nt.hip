@@ -10,7 +10,7 @@
 // 80 B apart (64 B of data + 16 B), so the 16 rows of an operand fragment
 // start on 16 different bank quadruples.
 #include "mla_device.h"
-#include "mla_internal.h"
+#include "mla_extra.h"
 
 namespace mla {
 namespace {

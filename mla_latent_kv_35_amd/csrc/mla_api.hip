@@ -4,7 +4,7 @@
 
 #include <algorithm>
 
-#include "mla_internal.h"
+#include "mla_extra.h"
 
 namespace mla {
 namespace {

@@ -18,7 +18,7 @@
 // with V^T read from LDS by the transposed read ds_read_b64_tr_b16.
 // Query i of a sequence sits at position n_kv - n_q + i and sees keys s <= it.
 #include "mla_device.h"
-#include "mla_internal.h"
+#include "mla_extra.h"
 
 namespace mla {
 namespace {
