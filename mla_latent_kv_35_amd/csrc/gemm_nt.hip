@@ -26,7 +26,19 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(const void* __restrict__ A
                                                       void* __restrict__ C, int M, int N, int K) {
   __shared__ __attribute__((aligned(16))) char smem_raw[4 * kBuf];   // A[2], B[2]
   lds_char* const smem = (lds_char*)smem_raw;
-  const int m0 = blockIdx.y * kTile, n0 = blockIdx.x * kTile;
+  // the row tiles of one block of B (weight rows) run on one XCD, which keeps
+  // that XCD's share of B in its L2 while all of A streams past it
+  const int n_mt = (M + kTile - 1) / kTile, n_nt = N / kTile;
+  int mt, nt;
+  if (n_nt % kNumXcd == 0) {
+    const int x = blockIdx.x % kNumXcd, idx = blockIdx.x / kNumXcd;
+    nt = kNumXcd * (idx / n_mt) + x;
+    mt = idx % n_mt;
+  } else {
+    nt = blockIdx.x / n_mt;
+    mt = blockIdx.x % n_mt;
+  }
+  const int m0 = mt * kTile, n0 = nt * kTile;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int i16 = lane & 15, G4 = lane >> 4;
   const int wm = w >> 1, wn = w & 1;
@@ -106,7 +118,7 @@ hipError_t launch_gemm_nt(const void* A, int a_bf16, const uint16_t* B, void* C,
                           int N, int K, hipStream_t s) {
   if (M == 0) return hipSuccess;
   if (N % kTile != 0 || K % kKc != 0) return hipErrorInvalidValue;
-  const dim3 grid(N / kTile, (M + kTile - 1) / kTile);
+  const dim3 grid((N / kTile) * ((M + kTile - 1) / kTile));
   if (a_bf16 && c_bf16)
     hipLaunchKernelGGL((gemm_nt_kernel<true, true>), grid, dim3(256), 0, s, A, B, C, M, N, K);
   else if (a_bf16)

@@ -51,10 +51,20 @@ __device__ __forceinline__ int v_byte(int t, int byte) {
 __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(16))) char smem_raw[kLds];
   lds_char* const smem = (lds_char*)smem_raw;
+  // every query block of one (sequence, head) runs on the same XCD, so that
+  // head's keys and values (2 MB at 4096 tokens) stay in that XCD's L2;
+  // within a head the blocks with the most keys (the last) go first
   const int n_qb = (p.n_q + kQBlock - 1) / kQBlock;
-  const int qb = blockIdx.x % n_qb;
-  const int h = (blockIdx.x / n_qb) % p.H;
-  const int b = blockIdx.x / (n_qb * p.H);
+  int bh, qb;
+  if ((p.B * p.H) % kNumXcd == 0) {
+    const int x = blockIdx.x % kNumXcd, idx = blockIdx.x / kNumXcd;
+    bh = kNumXcd * (idx / n_qb) + x;
+    qb = n_qb - 1 - idx % n_qb;
+  } else {
+    bh = blockIdx.x / n_qb;
+    qb = n_qb - 1 - blockIdx.x % n_qb;
+  }
+  const int h = bh % p.H, b = bh / p.H;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int i16 = lane & 15, G4 = lane >> 4;
   const int q0 = qb * kQBlock;
