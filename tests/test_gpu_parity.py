@@ -125,7 +125,8 @@ def test_small_fp32_parity(mla, split):
 @pytest.mark.parametrize("kw", SMALL)
 @pytest.mark.parametrize("split", [0, 64, 192])
 def test_small_fp8_parity(mla, kw, split):
-    # fp8 latent cache with per-token scales; the kernel also quantizes q_lat
+    # fp8 latent cache with per-token scales; the codes are widened exactly to
+    # bf16 for the MFMA and q_lat stays bf16
     cfg = synth.small_config(seed=300 + kw["B"] + kw["seq_len"], ckv_dt="fp8", **kw)
     check_against_oracle(mla, synth.make_inputs(cfg), split_tokens=split)
 
