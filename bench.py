@@ -1,6 +1,7 @@
 """Benchmark of the MLA absorbed-decode hot path on one MI355X.
 
-One step = the whole path over one batch: mla_absorb_q -> mla_rope ->
+One step = the whole path over one batch: mla_absorb_q_rope (the absorbed
+content query and the rotated rope query, one launch) ->
 mla_decode_paged (split kernel, then the log-sum-exp combine fused with the
 per-head value up-projection W_UV), on the
 DeepSeek-V2-shaped layer B=32, H=128, S=4096, bf16 (synthetic, seeded; see
@@ -137,8 +138,7 @@ def main():
 
     def step(i):
         c = caches[i % R]
-        mla.absorb_q(d.q_nope, d.w_uk, out=q_lat)
-        mla.rope(d.q_rope, d.positions, out=q_rot)
+        mla.absorb_q_rope(d.q_nope, d.w_uk, d.q_rope, d.positions, q_lat=q_lat, q_rot=q_rot)
         # the value up-projection runs inside the decode call (fused with the
         # log-sum-exp combine when the plan splits the sequences)
         mla.decode_paged(q_lat, q_rot, c, cfg.T, cfg.softmax_scale, out=u, lse=lse,

@@ -102,6 +102,27 @@ int mla_rope_freq(const void* x_in, void* x_out, int dt, const int32_t* pos,
                   int n_tok, int n_heads, int d_r, const double* theta, void* stream);
 
 /*
+ * mla_absorb_q_rope -- the query side of a decode step in one call: the
+ * result is exactly that of mla_absorb_q(q_nope, w_uk, q_lat, ...) followed
+ * by mla_rope(q_rope, q_rot, rope_dt, pos, ..., base) -- or by
+ * mla_rope_freq(..., theta) when theta is not NULL -- bit for bit. The two
+ * halves of the V2 analysis page's query (section 1.3, eq. 14-15: the
+ * absorbed content part and the separately rotated rope part) are
+ * independent, so with BF16 queries, BF16 rope data, d_r = 64 and 16-byte
+ * aligned rope rows they run as one kernel launch; otherwise as the two calls.
+ *   q_nope, w_uk, q_lat, q_dt, out_dt, d_h, d_c : as mla_absorb_q (n_tok x H)
+ *   q_rope, q_rot : [n_tok][H][d_r], dtype rope_dt (F32 or BF16); may alias
+ *   pos           : int32 [n_tok]
+ *   theta         : DEVICE fp64 [d_r / 2] or NULL (then base^(-2i/d_r))
+ * Errors: those of mla_absorb_q and mla_rope / mla_rope_freq; nothing is
+ * launched when any argument is rejected.
+ */
+int mla_absorb_q_rope(const void* q_nope, const void* w_uk, void* q_lat, int q_dt, int out_dt,
+                      const void* q_rope, void* q_rot, int rope_dt, const int32_t* pos,
+                      int n_tok, int H, int d_h, int d_c, int d_r, double base,
+                      const double* theta, void* stream);
+
+/*
  * mla_yarn_frequencies -- YaRN frequencies of the decoupled rope part for a
  * context extended by `factor` (V2 analysis page, section 3.2: YaRN acts on
  * the 64 rope dimensions only; V2 uses factor s = 40, alpha = 1, beta = 32 on

@@ -102,11 +102,14 @@ _lib.mla_cache_append.restype = _i
 _lib.mla_cache_append.argtypes = [ctypes.POINTER(AppendArgs), _vp]
 _lib.mla_out_proj.restype = _i
 _lib.mla_out_proj.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]
+_lib.mla_absorb_q_rope.restype = _i
+_lib.mla_absorb_q_rope.argtypes = [_vp, _vp, _vp, _i, _i, _vp, _vp, _i, _vp, _i, _i, _i, _i, _i,
+                                   _d, _vp, _vp]
 
 EXPORTED = ["mla_status_str", "mla_abi_version", "mla_absorb_q", "mla_rope",
             "mla_decode_plan", "mla_decode_paged", "mla_out_proj", "mla_cache_append",
             "mla_rope_freq", "mla_yarn_frequencies", "mla_yarn_mscale", "mla_expand_kv",
-            "mla_prefill_attn"]
+            "mla_prefill_attn", "mla_absorb_q_rope"]
 
 
 def lib():
@@ -183,6 +186,28 @@ def rope_freq(x: torch.Tensor, pos: torch.Tensor, theta: torch.Tensor,
     _check("mla_rope_freq", _lib.mla_rope_freq(_ptr(x), _ptr(out), dtype_code(x), _ptr(pos), n,
                                                heads, dr, _ptr(theta), _stream(stream)))
     return out
+
+
+def absorb_q_rope(q_nope: torch.Tensor, w_uk: torch.Tensor, q_rope: torch.Tensor,
+                  pos: torch.Tensor, base: float = 10000.0, theta: Optional[torch.Tensor] = None,
+                  out_dtype=None, q_lat: Optional[torch.Tensor] = None,
+                  q_rot: Optional[torch.Tensor] = None, stream=None):
+    """absorb_q then rope (or rope_freq when theta is given) as one call:
+    (q_lat [n, H, 512], q_rot [n, H, d_r])."""
+    n, H, dh = q_nope.shape
+    dc = w_uk.shape[2]
+    dr = q_rope.shape[2]
+    if q_lat is None:
+        q_lat = torch.empty((n, H, dc), dtype=out_dtype or q_nope.dtype, device=q_nope.device)
+    if q_rot is None:
+        q_rot = torch.empty_like(q_rope)
+    if theta is not None:
+        assert theta.dtype == torch.float64 and theta.numel() == dr // 2
+    _check("mla_absorb_q_rope", _lib.mla_absorb_q_rope(
+        _ptr(q_nope), _ptr(w_uk), _ptr(q_lat), dtype_code(q_nope), dtype_code(q_lat),
+        _ptr(q_rope), _ptr(q_rot), dtype_code(q_rope), _ptr(pos), n, H, dh, dc, dr, float(base),
+        _ptr(theta), _stream(stream)))
+    return q_lat, q_rot
 
 
 def expand_kv(c: torch.Tensor, w_uk: torch.Tensor, w_uv: torch.Tensor, out_dtype=None,
@@ -403,10 +428,16 @@ def upload(inp, device="cuda") -> DeviceInputs:
 def decode_step(d: DeviceInputs, split_tokens: int = 0, stream=None, rope_base: float = 10000.0,
                 fused: bool = True):
     """One pass of the whole hot path: absorb -> rope -> paged decode (+combine) -> out-proj.
-    fused: the projection runs inside mla_decode_paged (with the combine when
-    there are splits); otherwise as a separate mla_out_proj call."""
-    q_lat = absorb_q(d.q_nope, d.w_uk, stream=stream)
-    q_rot = rope(d.q_rope, d.positions, rope_base, stream=stream)
+    fused: absorb and rope run as one mla_absorb_q_rope call, and the
+    projection runs inside mla_decode_paged (with the combine when there are
+    splits); otherwise every step is its own call (mla_absorb_q, mla_rope,
+    mla_decode_paged, mla_out_proj)."""
+    if fused:
+        q_lat, q_rot = absorb_q_rope(d.q_nope, d.w_uk, d.q_rope, d.positions, rope_base,
+                                     stream=stream)
+    else:
+        q_lat = absorb_q(d.q_nope, d.w_uk, stream=stream)
+        q_rot = rope(d.q_rope, d.positions, rope_base, stream=stream)
     u_dtype = torch.float32 if q_lat.dtype == torch.float32 else torch.bfloat16
     if fused:
         u, lse, o = decode_paged(q_lat, q_rot, d.cache, d.T, d.softmax_scale, out_dtype=u_dtype,

@@ -8,7 +8,9 @@
 // (ds_read_b64_tr_b16) as the K-major MFMA operand; the queries are read
 // straight from global memory as the other operand. fp32: plain fp32 FMA.
 #include "mla_device.h"
+#include "mla_extra.h"
 #include "mla_internal.h"
+#include "rope_body.h"
 
 namespace mla {
 namespace {
@@ -18,15 +20,16 @@ constexpr int kTokTile = 32;
 
 __device__ __forceinline__ int swz16(int s) { return (s & 8) | ((s & 3) << 1) | ((s >> 2) & 1); }
 
+constexpr int kAbsorbLds = kDh * 256;   // the staged 128 x 128 bf16 weight block
+
 template <bool OUT_BF16>
-__global__ __launch_bounds__(kThreads) void absorb_bf16_kernel(const uint16_t* __restrict__ q,
-                                                               const uint16_t* __restrict__ wuk,
-                                                               void* __restrict__ out, int n_tok,
-                                                               int H, int n_tb) {
-  __shared__ __attribute__((aligned(16))) char smem_raw[kDh * 256];
-  lds_char* smem = (lds_char*)smem_raw;
-  // blocks on XCD x (= blockIdx % 8) serve the heads h with h % 8 == x
-  const int x = blockIdx.x % kNumXcd, idx = blockIdx.x / kNumXcd;
+__device__ __forceinline__ void absorb_bf16_block(int bid, lds_char* smem,
+                                                  const uint16_t* __restrict__ q,
+                                                  const uint16_t* __restrict__ wuk,
+                                                  void* __restrict__ out, int n_tok, int H,
+                                                  int n_tb) {
+  // blocks on XCD x (= bid % 8) serve the heads h with h % 8 == x
+  const int x = bid % kNumXcd, idx = bid / kNumXcd;
   const int per_head = 4 * n_tb;
   const int h = kNumXcd * (idx / per_head) + x;
   if (h >= H) return;
@@ -100,6 +103,35 @@ __global__ __launch_bounds__(kThreads) void absorb_bf16_kernel(const uint16_t* _
     }
 }
 
+template <bool OUT_BF16>
+__global__ __launch_bounds__(kThreads) void absorb_bf16_kernel(const uint16_t* __restrict__ q,
+                                                               const uint16_t* __restrict__ wuk,
+                                                               void* __restrict__ out, int n_tok,
+                                                               int H, int n_tb) {
+  __shared__ __attribute__((aligned(16))) char smem[kAbsorbLds];
+  absorb_bf16_block<OUT_BF16>(blockIdx.x, (lds_char*)smem, q, wuk, out, n_tok, H, n_tb);
+}
+
+// The query side of one decode step in one launch: the first n_abs blocks
+// absorb W_UK into the content queries exactly as absorb_bf16_kernel does,
+// the rest rotate the rope queries exactly as the d_r = 64 rope kernel does
+// (one block per token and 32 heads). The two halves touch disjoint buffers.
+// n_abs is a multiple of 8, so the absorb blocks keep their XCD placement.
+template <bool OUT_BF16>
+__global__ __launch_bounds__(kThreads) void absorb_rope_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ wuk, void* __restrict__ out,
+    int n_tok, int H, int n_tb, int n_abs, const uint16_t* q_rope, uint16_t* q_rot,
+    const int32_t* pos, double base, const double* freq) {
+  __shared__ __attribute__((aligned(16))) char smem[kAbsorbLds];   // either half's LDS
+  const int bid = blockIdx.x;
+  if (bid < n_abs) {
+    absorb_bf16_block<OUT_BF16>(bid, (lds_char*)smem, q, wuk, out, n_tok, H, n_tb);
+  } else {
+    const int r = bid - n_abs, n_hb = (H + kRope64Heads - 1) / kRope64Heads;
+    rope64_block<true>(r / n_hb, r % n_hb, (lds_char*)smem, q_rope, q_rot, pos, H, base, freq);
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void absorb_f32_kernel(const float* __restrict__ q,
                                                               const float* __restrict__ wuk,
                                                               float* __restrict__ out, int n_tok,
@@ -135,6 +167,25 @@ hipError_t launch_absorb(const void* q_nope, const void* w_uk, void* q_lat, int 
     hipLaunchKernelGGL(absorb_f32_kernel, dim3(n_tok * H), dim3(kThreads), 0, s,
                        (const float*)q_nope, (const float*)w_uk, (float*)q_lat, n_tok, H);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_absorb_rope(const uint16_t* q_nope, const uint16_t* w_uk, void* q_lat,
+                              int out_bf16, const uint16_t* q_rope, uint16_t* q_rot,
+                              const int32_t* pos, int n_tok, int H, double base,
+                              const double* freq, hipStream_t s) {
+  if (n_tok == 0) return hipSuccess;
+  const int n_tb = (n_tok + kTokTile - 1) / kTokTile;
+  const int n_abs = kNumXcd * ((H + kNumXcd - 1) / kNumXcd) * 4 * n_tb;
+  const int n_rope = n_tok * ((H + kRope64Heads - 1) / kRope64Heads);
+  static_assert(kRope64Threads == kThreads, "one block size for both halves");
+  const dim3 grid(n_abs + n_rope);
+  if (out_bf16)
+    hipLaunchKernelGGL(absorb_rope_kernel<true>, grid, dim3(kThreads), 0, s, q_nope, w_uk, q_lat,
+                       n_tok, H, n_tb, n_abs, q_rope, q_rot, pos, base, freq);
+  else
+    hipLaunchKernelGGL(absorb_rope_kernel<false>, grid, dim3(kThreads), 0, s, q_nope, w_uk, q_lat,
+                       n_tok, H, n_tb, n_abs, q_rope, q_rot, pos, base, freq);
   return hipGetLastError();
 }
 

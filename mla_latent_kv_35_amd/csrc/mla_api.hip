@@ -148,6 +148,34 @@ int mla_rope_freq(const void* x_in, void* x_out, int dt, const int32_t* pos, int
   return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
 }
 
+int mla_absorb_q_rope(const void* q_nope, const void* w_uk, void* q_lat, int q_dt, int out_dt,
+                      const void* q_rope, void* q_rot, int rope_dt, const int32_t* pos,
+                      int n_tok, int H, int d_h, int d_c, int d_r, double base,
+                      const double* theta, void* stream) {
+  if (n_tok < 0 || H < 1) return MLA_ERR_SHAPE;
+  if (d_h != kDh || d_c != kDc) return MLA_ERR_UNSUPPORTED;
+  if (d_r < 2 || d_r > 256 || d_r % 2 != 0) return MLA_ERR_UNSUPPORTED;
+  if (!is_float_dt(q_dt) || !is_float_dt(out_dt) || !is_float_dt(rope_dt)) return MLA_ERR_DTYPE;
+  if (q_dt == MLA_F32 && out_dt != MLA_F32) return MLA_ERR_DTYPE;
+  if (!theta && (!(base > 0.0) || !isfinite(base))) return MLA_ERR_SHAPE;
+  if (n_tok == 0) return MLA_OK;
+  if (!q_nope || !w_uk || !q_lat || !q_rope || !q_rot || !pos) return MLA_ERR_NULL;
+  const hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (q_dt == MLA_BF16 && rope_dt == MLA_BF16 && d_r == 64 &&
+      (((uintptr_t)q_rope | (uintptr_t)q_rot) & 15) == 0) {
+    e = launch_absorb_rope((const uint16_t*)q_nope, (const uint16_t*)w_uk, q_lat,
+                           out_dt == MLA_BF16, (const uint16_t*)q_rope, (uint16_t*)q_rot, pos,
+                           n_tok, H, theta ? 1.0 : base, theta, s);
+  } else {
+    e = launch_absorb(q_nope, w_uk, q_lat, q_dt == MLA_BF16, out_dt == MLA_BF16, n_tok, H, s);
+    if (e == hipSuccess)
+      e = launch_rope(q_rope, q_rot, rope_dt == MLA_BF16, pos, n_tok, H, d_r, theta ? 1.0 : base,
+                      theta, s);
+  }
+  return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
+}
+
 int mla_yarn_frequencies(int d_r, double base, double factor, double alpha, double beta,
                          int orig_len, double* theta) {
   if (!theta) return MLA_ERR_NULL;

@@ -44,5 +44,11 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t s);
 // C[M][N] = A[M][K] B[N][K]^T, B bf16, A f32 or bf16; N % 128 == 0, K % 32 == 0
 hipError_t launch_gemm_nt(const void* A, int a_bf16, const uint16_t* B, void* C, int c_bf16, int M,
                           int N, int K, hipStream_t s);
+// absorb (bf16 queries, bf16 W_UK) and d_r = 64 bf16 rope in one launch;
+// freq null = base^(-2i/64)
+hipError_t launch_absorb_rope(const uint16_t* q_nope, const uint16_t* w_uk, void* q_lat,
+                              int out_bf16, const uint16_t* q_rope, uint16_t* q_rot,
+                              const int32_t* pos, int n_tok, int H, double base,
+                              const double* freq, hipStream_t s);
 
 }  // namespace mla

@@ -160,3 +160,18 @@ def test_rope_freq_rejects_before_launch(B):
     assert L.mla_rope_freq(None, None, 1, None, 4, 128, 64, None, None) == 1
     assert L.mla_rope_freq(None, None, 1, None, 0, 128, 64, None, None) == 0    # empty: no-op
     assert L.mla_rope_freq(None, None, 1, None, -1, 128, 64, None, None) == 2
+
+
+def test_absorb_q_rope_rejects_before_launch(B):
+    L = B.lib()
+    f = L.mla_absorb_q_rope
+    # (q_nope, w_uk, q_lat, q_dt, out_dt, q_rope, q_rot, rope_dt, pos, n_tok, H, d_h, d_c, d_r,
+    #  base, theta, stream)
+    assert f(None, None, None, 1, 1, None, None, 1, None, 4, 128, 128, 512, 64, 1e4, None, None) == 1
+    assert f(None, None, None, 1, 1, None, None, 1, None, 4, 128, 64, 512, 64, 1e4, None, None) == 4
+    assert f(None, None, None, 1, 1, None, None, 1, None, 4, 128, 128, 512, 63, 1e4, None, None) == 4
+    assert f(None, None, None, 0, 1, None, None, 1, None, 4, 128, 128, 512, 64, 1e4, None, None) == 3
+    assert f(None, None, None, 1, 1, None, None, 2, None, 4, 128, 128, 512, 64, 1e4, None, None) == 3
+    assert f(None, None, None, 1, 1, None, None, 1, None, 4, 128, 128, 512, 64, -1., None, None) == 2
+    assert f(None, None, None, 1, 1, None, None, 1, None, -1, 128, 128, 512, 64, 1e4, None, None) == 2
+    assert f(None, None, None, 1, 1, None, None, 1, None, 0, 128, 128, 512, 64, 1e4, None, None) == 0
