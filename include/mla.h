@@ -331,8 +331,9 @@ int mla_expand_kv(const void* c, const void* w_uk, const void* w_uv, void* k_nop
  *   v      : [B][n_kv][H][d_h] BF16
  *   o      : [B][n_q][H][d_h]  dtype o_dt (F32 or BF16)
  *   lse    : [B][n_q][H] fp32 natural-log sum of exp(scores), or NULL
- * Supported: d_h = 128, d_r = 64, 1 <= n_q <= n_kv, 16-byte aligned tensors.
- * bf16 MFMA, fp32 softmax and accumulation.
+ * Supported: d_h = 128, d_r = 64, 1 <= n_q <= n_kv, H <= 65536, 16-byte
+ * aligned tensors (else MLA_ERR_UNSUPPORTED). bf16 MFMA, fp32 softmax and
+ * accumulation.
  */
 int mla_prefill_attn(const void* q_nope, const void* q_rope, const void* k_nope,
                      const void* k_rope, const void* v, void* o, float* lse, int o_dt, int B,

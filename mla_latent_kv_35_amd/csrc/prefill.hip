@@ -5,50 +5,51 @@
 // arithmetic it is the same function as the absorbed decode form).
 //
 // Causal flash attention, d_qk = 192, d_v = 128, bf16 inputs, fp32
-// accumulation. One workgroup of 4 waves per (sequence b, head h, 64
-// queries); wave w owns queries 16w..16w+15 of the block and keeps their 192
-// query values in registers. Keys and values stream through LDS in tiles of
-// 64 keys (register-staged, the next tile's loads in flight during the
-// current tile's math). Per 16-key block a wave computes
+// accumulation. One workgroup of 4 waves per (sequence b, head h, 128
+// queries); wave w owns queries 32w..32w+31 of the block (two 16-query
+// columns) and keeps their 192 query values in registers, so every key or
+// value fragment read from LDS feeds two MFMAs. Keys and values stream
+// through LDS in tiles of 64 keys, double-buffered: the next tile's direct
+// global -> LDS copies are in flight during the current tile's math, with
+// one workgroup barrier per tile. Per 16-key block a wave computes
 //   S^T[key][query] = K[key][:] . Q^T   on v_mfma_f32_16x16x32_bf16,
-// so each lane holds 4 keys x 1 query; after the online softmax (log2
-// domain, scale folded into the exponent) those 4 probabilities are exactly
-// the B operand of
-//   O^T[dv][query] += V^T[dv][key] . P^T[key][query]   on v_mfma_f32_16x16x16_bf16,
-// with V^T read from LDS by the transposed read ds_read_b64_tr_b16.
+// so each lane holds 4 keys x 1 query. After the online softmax (log2
+// domain, scale folded into the exponent) the lane's 4 + 4 probabilities of
+// key blocks 2kk and 2kk+1 are taken as K elements 0..7 of
+//   O^T[dv][query] += V^T[dv][key] . P^T[key][query]   on v_mfma_f32_16x16x32_bf16
+// (a K order of our choosing: the V^T operand is read in the same order by
+// two transposed reads ds_read_b64_tr_b16, keys 4g..4g+3 and 16+4g..16+4g+3).
 // Query i of a sequence sits at position n_kv - n_q + i and sees keys s <= it.
 #include "mla_device.h"
+#include "dma.h"
 #include "mla_extra.h"
 
 namespace mla {
 namespace {
 
-constexpr int kQBlock = 64;
-constexpr int kKTile = 64;
+constexpr int kQBlock = 128;                      // queries per workgroup, 32 per wave
+constexpr int kKTile = 64;                        // keys per tile
 constexpr int kThreads = 256;
-constexpr int kRow = 256;                       // bytes per key row in each LDS region
-constexpr int kOffKr = kKTile * kRow;           // k_nope [64][256 B], then k_rope, then V
-constexpr int kOffV = 2 * kKTile * kRow;
-constexpr int kLds = 3 * kKTile * kRow;         // 48 KB
+constexpr int kKRow = 256;                        // bytes per k_nope / V row in LDS
+constexpr int kRRow = 128;                        // bytes per k_rope row in LDS
+constexpr int kOffKr = kKTile * kKRow;            // k_nope [64][256 B], k_rope [64][128 B], V
+constexpr int kOffV = kOffKr + kKTile * kRRow;
+constexpr int kBuf = kOffV + kKTile * kKRow;      // one tile: 40 KB
+constexpr int kLds = 2 * kBuf;                    // two tiles: 80 KB (two workgroups per CU)
 
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ f32x4_t mfma16x16x16(const bf16x4_t& a, const bf16x4_t& b,
-                                                const f32x4_t& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a),
-                                                   __builtin_bit_cast(s16x4_t, b), c, 0, 0, 0);
-}
-
-// K rows (k_nope, and k_rope padded to 256 B): 16-B chunk c of key t lives at
-// chunk c ^ (t & 15), so the 16 keys of an MFMA A fragment read 16 distinct
-// chunks. V rows: 32-B block n (16 dv) of key t lives at block n ^ (t & 7),
-// so the transposed reads of 8 consecutive keys hit distinct banks.
-__device__ __forceinline__ int k_chunk(int t, int c) { return ((c ^ (t & 15)) << 4); }
+// K rows: 16-B chunk c of key t lives at chunk c ^ (t & 15), so the 16 keys
+// of an MFMA A fragment read 16 distinct chunks. Rope rows (128 B): chunk c
+// at c ^ ((t >> 1) & 7), which spreads 16 consecutive keys over 256 B. V
+// rows: 32-B block n (16 dv) of key t lives at block n ^ (t & 7), so the
+// transposed reads of 8 consecutive keys hit distinct banks.
+__device__ __forceinline__ int k_pos(int t, int c) { return c ^ (t & 15); }
+__device__ __forceinline__ int r_pos(int t, int c) { return c ^ ((t >> 1) & 7); }
 __device__ __forceinline__ int v_byte(int t, int byte) {
   return (((byte >> 5) ^ (t & 7)) << 5) | (byte & 31);
 }
 
-__global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(16))) char smem_raw[kLds];
   lds_char* const smem = (lds_char*)smem_raw;
   // every query block of one (sequence, head) runs on the same XCD, so that
@@ -65,158 +66,199 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     qb = n_qb - 1 - blockIdx.x % n_qb;
   }
   const int h = bh % p.H, b = bh / p.H;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int i16 = lane & 15, G4 = lane >> 4;
   const int q0 = qb * kQBlock;
   const int shift = p.n_kv - p.n_q;              // position of query i is shift + i
   const int kv_end = min(p.n_kv, shift + min(q0 + kQBlock, p.n_q));   // keys this block needs
   const int n_tiles = (kv_end + kKTile - 1) / kKTile;
+  // this wave's queries: [wq0, wq1]; a wave past the end only copies
+  const int wq0 = q0 + 32 * w;
+  const int wq1 = min(wq0 + 31, p.n_q - 1);
+  const bool active = wq0 < p.n_q;
 
-  // this wave's queries as MFMA B fragments: 4 k-steps of q_nope, 2 of q_rope
-  const int qi = q0 + 16 * w + i16;              // this lane's query (B column)
-  bf16x8_t qf[6];
+  // copy duties per tile (keys 16w..16w+15 of the tile): 4 x 1 KB of k_nope,
+  // 2 x 1 KB of k_rope, 4 x 1 KB of V; the lane's global chunk is the one the
+  // swizzled layout puts at its LDS slot
+  const size_t head_stride = (size_t)p.H * kKRow;                  // bytes between keys
+  const char* const kn_base = (const char*)p.k_nope + ((size_t)b * p.n_kv * p.H + h) * kKRow;
+  const char* const v_base = (const char*)p.v + ((size_t)b * p.n_kv * p.H + h) * kKRow;
+  const char* const kr_base = (const char*)p.k_rope + (size_t)b * p.n_kv * kRRow;
+  auto issue_tile = [&](int tile) __attribute__((always_inline)) {
+    const int t0 = tile * kKTile;
+    const int last = p.n_kv - 1 - t0;            // keys past the end read the last key
+    lds_char* const buf = smem + (tile & 1) * kBuf;
+    const char* const kn = kn_base + (size_t)t0 * head_stride;
+    const char* const vv = v_base + (size_t)t0 * head_stride;
+    const char* const kr = kr_base + (size_t)t0 * kRRow;
 #pragma unroll
-  for (int ks = 0; ks < 6; ++ks) qf[ks] = (bf16x8_t){0, 0, 0, 0, 0, 0, 0, 0};
-  if (qi < p.n_q) {
-    const size_t row = ((size_t)b * p.n_q + qi) * p.H + h;
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * w + 4 * i + (lane >> 4), slot = lane & 15;
+      const uint32_t row = (uint32_t)min(t, last) * (uint32_t)head_stride;
+      dma_copy16(kn, row + 16 * k_pos(t, slot), buf + (16 * w + 4 * i) * kKRow);
+      const int vb = ((slot >> 1) ^ (t & 7)) * 2 + (slot & 1);   // V chunk for this slot
+      dma_copy16(vv, row + 16 * vb, buf + kOffV + (16 * w + 4 * i) * kKRow);
+    }
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qf[ks] = load_bf16x8((const uint16_t*)p.q_nope + row * kDh + 32 * ks + 8 * G4);
+    for (int i = 0; i < 2; ++i) {
+      const int t = 16 * w + 8 * i + (lane >> 3), slot = lane & 7;
+      dma_copy16(kr, (uint32_t)min(t, last) * kRRow + 16 * r_pos(t, slot),
+                 buf + kOffKr + (16 * w + 8 * i) * kRRow);
+    }
+  };
+  if (n_tiles > 0) issue_tile(0);
+
+  // this wave's queries as MFMA B fragments: [column][4 k-steps of q_nope, 2 of q_rope]
+  bf16x8_t qf[2][6];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) qf[4 + ks] = load_bf16x8((const uint16_t*)p.q_rope + row * kDr + 32 * ks + 8 * G4);
+  for (int cb = 0; cb < 2; ++cb) {
+    const int qi = wq0 + 16 * cb + i16;
+#pragma unroll
+    for (int ks = 0; ks < 6; ++ks) qf[cb][ks] = (bf16x8_t){0, 0, 0, 0, 0, 0, 0, 0};
+    if (qi < p.n_q) {
+      const size_t row = ((size_t)b * p.n_q + qi) * p.H + h;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        qf[cb][ks] = load_bf16x8((const uint16_t*)p.q_nope + row * kDh + 32 * ks + 8 * G4);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        qf[cb][4 + ks] = load_bf16x8((const uint16_t*)p.q_rope + row * kDr + 32 * ks + 8 * G4);
+    }
   }
-  const int qpos = shift + qi;                   // causal limit of this lane's query
 
-  // cooperative tile loads: 4 k_nope + 2 k_rope + 4 V chunks of 16 B per thread
-  u32x4_t stg[10];
-  auto load_tile = [&](int t0) __attribute__((always_inline)) {
+  f32x4_t o[8][2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = tid + kThreads * i, t = e >> 4, c = e & 15;
-      const int s = t0 + t;
-      stg[i] = (u32x4_t){0u, 0u, 0u, 0u};
-      stg[6 + i] = (u32x4_t){0u, 0u, 0u, 0u};
-      if (s < p.n_kv) {
-        const size_t kv = ((size_t)b * p.n_kv + s) * p.H + h;
-        stg[i] = *(const u32x4_t*)((const uint16_t*)p.k_nope + kv * kDh + 8 * c);
-        stg[6 + i] = *(const u32x4_t*)((const uint16_t*)p.v + kv * kDh + 8 * c);
-      }
-    }
+  for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int e = tid + kThreads * i, t = e >> 3, c = e & 7;
-      const int s = t0 + t;
-      stg[4 + i] = (u32x4_t){0u, 0u, 0u, 0u};
-      if (s < p.n_kv)
-        stg[4 + i] = *(const u32x4_t*)((const uint16_t*)p.k_rope + ((size_t)b * p.n_kv + s) * kDr + 8 * c);
-    }
-  };
-  auto store_tile = [&]() __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = tid + kThreads * i, t = e >> 4, c = e & 15;
-      *(MLA_LDS u32x4_t*)(smem + t * kRow + k_chunk(t, c)) = stg[i];
-      *(MLA_LDS u32x4_t*)(smem + kOffV + t * kRow + v_byte(t, 16 * c)) = stg[6 + i];
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int e = tid + kThreads * i, t = e >> 3, c = e & 7;
-      *(MLA_LDS u32x4_t*)(smem + kOffKr + t * kRow + k_chunk(t, c)) = stg[4 + i];
-    }
-  };
-
-  f32x4_t o[8];
-#pragma unroll
-  for (int nb = 0; nb < 8; ++nb) o[nb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, l = 0.f;                  // this lane's query (column i16)
+    for (int cb = 0; cb < 2; ++cb) o[nb][cb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};   // this lane's two queries
   const float sl2 = p.scale_log2;
 
-  if (n_tiles > 0) {
-    load_tile(0);
-    store_tile();
-  }
-  __syncthreads();
   for (int tile = 0; tile < n_tiles; ++tile) {
     const int t0 = tile * kKTile;
-    if (tile + 1 < n_tiles) load_tile(t0 + kKTile);
-    // ---- scores S^T for the 4 key blocks of the tile
-    f32x4_t s[4];
+    dma_wait<0>();                               // this wave's copies of tile `tile` landed
+    lds_barrier();                               // all copies landed; tile-1's buffer is free
+    if (tile + 1 < n_tiles) issue_tile(tile + 1);
+    // keys past the wave's last query are masked for all of its queries
+    if (!active || t0 > shift + wq1) continue;
+    const lds_char* const kt = smem + (tile & 1) * kBuf;
+    const lds_char* const vt = kt + kOffV;
+    // ---- scores S^T for the 4 key blocks of the tile and both query columns
+    // fragment f = (key block f / 6, k-step f % 6); a ring of kRing reads
+    // stays in flight ahead of the MFMAs that consume them
+    f32x4_t s[4][2];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      s[kb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-      const int t = 16 * kb + i16;               // this lane's key (A row)
+    for (int kb = 0; kb < 4; ++kb) s[kb][0] = s[kb][1] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    auto kfrag = [&](int f) __attribute__((always_inline)) -> bf16x8_t {
+      const int t = 16 * (f / 6) + i16, ks = f % 6;   // this lane's key (A row), k-step
+      return lds_read_b128(ks < 4 ? kt + t * kKRow + 16 * k_pos(t, 4 * ks + G4)
+                                  : kt + kOffKr + t * kRRow + 16 * r_pos(t, 4 * (ks - 4) + G4));
+    };
+    constexpr int kRing = 6;
+    bf16x8_t ring[kRing];
 #pragma unroll
-      for (int ks = 0; ks < 6; ++ks) {
-        const lds_char* a = ks < 4 ? smem + t * kRow + k_chunk(t, 4 * ks + G4)
-                                   : smem + kOffKr + t * kRow + k_chunk(t, 4 * (ks - 4) + G4);
-        s[kb] = mfma16x16x32(lds_read_b128(a), qf[ks], s[kb]);
+    for (int f = 0; f < kRing; ++f) ring[f] = kfrag(f);
+    __builtin_amdgcn_sched_group_barrier(0x100, kRing, 0);
+#pragma unroll
+    for (int f = 0; f < 24; ++f) {
+      const bf16x8_t af = ring[f % kRing];
+      if (f + kRing < 24) ring[f % kRing] = kfrag(f + kRing);
+      s[f / 6][0] = mfma16x16x32(af, qf[0][f % 6], s[f / 6][0]);
+      s[f / 6][1] = mfma16x16x32(af, qf[1][f % 6], s[f / 6][1]);
+      if (f + kRing < 24) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    }
+    // ---- V^T fragments for O^T += V^T P^T (two 32-key steps): fragment
+    // f = (step f / 8, dv block f % 8), two transposed reads each; the first
+    // kVRing are read now, under the softmax, the rest kVRing ahead of use
+    auto vfrag = [&](int f) __attribute__((always_inline)) -> bf16x8_t {
+      const int tl = 32 * (f / 8) + 4 * G4 + (i16 >> 2);   // key row this lane addresses
+      const int th = tl + 16;
+      const int byte = 32 * (f % 8) + 8 * (i16 & 3);
+      return concat(lds_read_tr16(vt + tl * kKRow + v_byte(tl, byte)),
+                    lds_read_tr16(vt + th * kKRow + v_byte(th, byte)));
+    };
+    constexpr int kVRing = 4;
+    bf16x8_t vring[kVRing];
+#pragma unroll
+    for (int f = 0; f < kVRing; ++f) vring[f] = vfrag(f);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kVRing, 0);
+    // ---- causal mask (only tiles that reach past the wave's first query)
+    if (t0 + kKTile - 1 > shift + wq0) {
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        const int qpos = shift + wq0 + 16 * cb + i16;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (t0 + 16 * kb + 4 * G4 + i > qpos) s[kb][cb][i] = -INFINITY;
       }
     }
-    // ---- causal mask (only tiles that reach past the block's first query)
-    if (t0 + kKTile - 1 > shift + q0) {
+    // ---- online softmax per query (its keys are spread over lanes l, l^16, l^32, l^48)
+    bf16x4_t pb[4][2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      float mt = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (t0 + 16 * kb + 4 * G4 + i > qpos) s[kb][i] = -INFINITY;
-    }
-    // ---- online softmax for this lane's query (keys spread over lanes l, l^16, l^32, l^48)
-    float mt = -INFINITY;
+        for (int i = 0; i < 4; ++i) mt = fmaxf(mt, s[kb][cb][i]);
+      mt = wave_max16(mt);
+      const float mnew = fmaxf(m[cb], mt * sl2);
+      const float base = mnew == -INFINITY ? 0.f : mnew;
+      const float alpha = m[cb] == -INFINITY ? 0.f : fast_exp2(m[cb] - base);
+      m[cb] = mnew;
+      float ls = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mt = fmaxf(mt, s[kb][i]);
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float mnew = fmaxf(m, mt * sl2);
-    const float base = mnew == -INFINITY ? 0.f : mnew;
-    const float alpha = m == -INFINITY ? 0.f : exp2f(m - base);
-    m = mnew;
-    bf16x4_t pb[4];
-    float ls = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const uint32_t lo = pack_bf16x2(exp2f(fmaf(s[kb][0], sl2, -base)), exp2f(fmaf(s[kb][1], sl2, -base)));
-      const uint32_t hi = pack_bf16x2(exp2f(fmaf(s[kb][2], sl2, -base)), exp2f(fmaf(s[kb][3], sl2, -base)));
-      ls += (bf2f(lo & 0xffff) + bf2f(lo >> 16)) + (bf2f(hi & 0xffff) + bf2f(hi >> 16));
-      pb[kb] = __builtin_bit_cast(bf16x4_t, (u32x2_t){lo, hi});
-    }
-    ls += __shfl_xor(ls, 16);
-    ls += __shfl_xor(ls, 32);
-    l = l * alpha + ls;
-#pragma unroll
-    for (int nb = 0; nb < 8; ++nb) o[nb] *= alpha;
-    // ---- O^T += V^T P^T over the 4 key blocks
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const int t = 16 * kb + 4 * G4 + (i16 >> 2);   // the key row this lane addresses
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
-        const bf16x4_t vt = lds_read_tr16(smem + kOffV + t * kRow + v_byte(t, 32 * nb + 8 * (i16 & 3)));
-        o[nb] = mfma16x16x16(vt, pb[kb], o[nb]);
+      for (int kb = 0; kb < 4; ++kb) {
+        const uint32_t lo = pack_bf16x2(fast_exp2(fmaf(s[kb][cb][0], sl2, -base)),
+                                        fast_exp2(fmaf(s[kb][cb][1], sl2, -base)));
+        const uint32_t hi = pack_bf16x2(fast_exp2(fmaf(s[kb][cb][2], sl2, -base)),
+                                        fast_exp2(fmaf(s[kb][cb][3], sl2, -base)));
+        ls += (bf2f(lo & 0xffff) + bf2f(lo >> 16)) + (bf2f(hi & 0xffff) + bf2f(hi >> 16));
+        pb[kb][cb] = __builtin_bit_cast(bf16x4_t, (u32x2_t){lo, hi});
       }
+      l[cb] = l[cb] * alpha + wave_sum16(ls);
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) o[nb][cb] *= alpha;
     }
-    __syncthreads();                             // every wave is done with this tile
-    if (tile + 1 < n_tiles) {
-      store_tile();
-      __syncthreads();
+    // ---- O^T += V^T P^T
+    bf16x8_t pB[2][2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) pB[kk][cb] = concat(pb[2 * kk][cb], pb[2 * kk + 1][cb]);
+#pragma unroll
+    for (int f = 0; f < 16; ++f) {
+      const bf16x8_t va = vring[f % kVRing];
+      if (f + kVRing < 16) vring[f % kVRing] = vfrag(f + kVRing);
+      o[f % 8][0] = mfma16x16x32(va, pB[f / 8][0], o[f % 8][0]);
+      o[f % 8][1] = mfma16x16x32(va, pB[f / 8][1], o[f % 8][1]);
+      if (f + kVRing < 16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     }
   }
 
-  // ---- finish: lane holds O^T[dv 16nb + 4*G4 + i][query qi]
-  if (qi < p.n_q) {
+  // ---- finish: lane holds O^T[dv 16nb + 4*G4 + i][query wq0 + 16cb + i16]
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const int qi = wq0 + 16 * cb + i16;
+    if (qi >= p.n_q) continue;
     const size_t row = ((size_t)b * p.n_q + qi) * p.H + h;
-    const float inv = 1.f / l;
+    const float inv = 1.f / l[cb];
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) {
       const size_t off = row * kDh + 16 * nb + 4 * G4;
+      const f32x4_t r = o[nb][cb] * inv;
       if (p.o_bf16) {
-        *(u32x2_t*)((uint16_t*)p.o + off) =
-            (u32x2_t){pack_bf16x2(o[nb][0] * inv, o[nb][1] * inv), pack_bf16x2(o[nb][2] * inv, o[nb][3] * inv)};
+        *(u32x2_t*)((uint16_t*)p.o + off) = (u32x2_t){pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
       } else {
-        *(f32x4_t*)((float*)p.o + off) = o[nb] * inv;
+        *(f32x4_t*)((float*)p.o + off) = r;
       }
     }
-    if (p.lse && G4 == 0) p.lse[row] = (m + log2f(l)) * kLn2;
+    if (p.lse && G4 == 0) p.lse[row] = (m[cb] + log2f(l[cb])) * kLn2;
   }
 }
 
