@@ -14,7 +14,7 @@
 // one workgroup barrier per tile. Per 16-key block a wave computes
 //   S^T[key][query] = K[key][:] . Q^T   on v_mfma_f32_16x16x32_bf16,
 // so each lane holds 4 keys x 1 query. After the online softmax (log2
-// domain, scale folded into the exponent) the lane's 4 + 4 probabilities of
+// domain, scale folded into the exponent, lazily moved maximum) the lane's 4 + 4 probabilities of
 // key blocks 2kk and 2kk+1 are taken as K elements 0..7 of
 //   O^T[dv][query] += V^T[dv][key] . P^T[key][query]   on v_mfma_f32_16x16x32_bf16
 // (a K order of our choosing: the V^T operand is read in the same order by
@@ -36,6 +36,12 @@ constexpr int kOffKr = kKTile * kKRow;            // k_nope [64][256 B], k_rope 
 constexpr int kOffV = kOffKr + kKTile * kRRow;
 constexpr int kBuf = kOffV + kKTile * kKRow;      // one tile: 40 KB
 constexpr int kLds = 2 * kBuf;                    // two tiles: 80 KB (two workgroups per CU)
+// The running maximum of a query moves only when a tile's maximum exceeds it
+// by more than this (log2 units): weights stay below 2^8, and the O rescale
+// is skipped for the many tiles that do not move it.
+constexpr float kLazyMax = 8.0f;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // K rows: 16-B chunk c of key t lives at chunk c ^ (t & 15), so the 16 keys
 // of an MFMA A fragment read 16 distinct chunks. Rope rows (128 B): chunk c
@@ -85,27 +91,38 @@ void prefill_kernel(PrefillParams p) {
   const char* const kn_base = (const char*)p.k_nope + ((size_t)b * p.n_kv * p.H + h) * kKRow;
   const char* const v_base = (const char*)p.v + ((size_t)b * p.n_kv * p.H + h) * kKRow;
   const char* const kr_base = (const char*)p.k_rope + (size_t)b * p.n_kv * kRRow;
+  // per-lane byte offsets of the copies within a tile; keys past the end of
+  // the sequence (only in its last tile) read the last key instead
+  uint32_t off_k[4], off_v[4], off_r[2];
+  auto copy_offsets = [&](int last) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * w + 4 * i + (lane >> 4), slot = lane & 15;
+      const uint32_t row = (uint32_t)min(t, last) * (uint32_t)head_stride;
+      off_k[i] = row + 16 * k_pos(t, slot);
+      off_v[i] = row + 16 * (((slot >> 1) ^ (t & 7)) * 2 + (slot & 1));   // V chunk of this slot
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int t = 16 * w + 8 * i + (lane >> 3), slot = lane & 7;
+      off_r[i] = (uint32_t)min(t, last) * kRRow + 16 * r_pos(t, slot);
+    }
+  };
+  copy_offsets(kKTile - 1);
   auto issue_tile = [&](int tile) __attribute__((always_inline)) {
     const int t0 = tile * kKTile;
-    const int last = p.n_kv - 1 - t0;            // keys past the end read the last key
+    if (t0 + kKTile > p.n_kv) copy_offsets(p.n_kv - 1 - t0);
     lds_char* const buf = smem + (tile & 1) * kBuf;
     const char* const kn = kn_base + (size_t)t0 * head_stride;
     const char* const vv = v_base + (size_t)t0 * head_stride;
     const char* const kr = kr_base + (size_t)t0 * kRRow;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int t = 16 * w + 4 * i + (lane >> 4), slot = lane & 15;
-      const uint32_t row = (uint32_t)min(t, last) * (uint32_t)head_stride;
-      dma_copy16(kn, row + 16 * k_pos(t, slot), buf + (16 * w + 4 * i) * kKRow);
-      const int vb = ((slot >> 1) ^ (t & 7)) * 2 + (slot & 1);   // V chunk for this slot
-      dma_copy16(vv, row + 16 * vb, buf + kOffV + (16 * w + 4 * i) * kKRow);
+      dma_copy16(kn, off_k[i], buf + (16 * w + 4 * i) * kKRow);
+      dma_copy16(vv, off_v[i], buf + kOffV + (16 * w + 4 * i) * kKRow);
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int t = 16 * w + 8 * i + (lane >> 3), slot = lane & 7;
-      dma_copy16(kr, (uint32_t)min(t, last) * kRRow + 16 * r_pos(t, slot),
-                 buf + kOffKr + (16 * w + 8 * i) * kRRow);
-    }
+    for (int i = 0; i < 2; ++i) dma_copy16(kr, off_r[i], buf + kOffKr + (16 * w + 8 * i) * kRRow);
   };
   if (n_tiles > 0) issue_tile(0);
 
@@ -205,24 +222,30 @@ void prefill_kernel(PrefillParams p) {
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) mt = fmaxf(mt, s[kb][cb][i]);
-      mt = wave_max16(mt);
-      const float mnew = fmaxf(m[cb], mt * sl2);
+      mt = wave_max16(mt) * sl2;
+      const float mold = m[cb];
+      const float mnew = (mt - mold > kLazyMax) ? mt : mold;   // -inf - -inf is NaN: keep
       const float base = mnew == -INFINITY ? 0.f : mnew;
-      const float alpha = m[cb] == -INFINITY ? 0.f : fast_exp2(m[cb] - base);
+      const float alpha = mnew == mold ? 1.f : fast_exp2(mold - mnew);
       m[cb] = mnew;
+      // row sum of the bf16-rounded weights (the values the MFMA multiplies)
       float ls = 0.f;
+      const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         const uint32_t lo = pack_bf16x2(fast_exp2(fmaf(s[kb][cb][0], sl2, -base)),
                                         fast_exp2(fmaf(s[kb][cb][1], sl2, -base)));
         const uint32_t hi = pack_bf16x2(fast_exp2(fmaf(s[kb][cb][2], sl2, -base)),
                                         fast_exp2(fmaf(s[kb][cb][3], sl2, -base)));
-        ls += (bf2f(lo & 0xffff) + bf2f(lo >> 16)) + (bf2f(hi & 0xffff) + bf2f(hi >> 16));
+        ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, lo), ones, ls, false);
+        ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, hi), ones, ls, false);
         pb[kb][cb] = __builtin_bit_cast(bf16x4_t, (u32x2_t){lo, hi});
       }
       l[cb] = l[cb] * alpha + wave_sum16(ls);
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb) o[nb][cb] *= alpha;
+        for (int nb = 0; nb < 8; ++nb) o[nb][cb] *= alpha;
+      }
     }
     // ---- O^T += V^T P^T
     bf16x8_t pB[2][2];
