@@ -343,7 +343,7 @@ int mla_prefill_attn(const void* q_nope, const void* q_rope, const void* k_nope,
   if (!is_float_dt(o_dt)) return MLA_ERR_DTYPE;
   if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return MLA_ERR_SHAPE;
   // the kernel's per-lane copy offsets (63 keys x H x 256 B) are 32-bit
-  if (H > 65536 || (int64_t)B * H * ((n_q + 127) / 128) > INT32_MAX) return MLA_ERR_UNSUPPORTED;
+  if (H > 65536 || (int64_t)B * H * ((n_q + 255) / 256) > INT32_MAX) return MLA_ERR_UNSUPPORTED;
   if (!q_nope || !q_rope || !k_nope || !k_rope || !v || !o) return MLA_ERR_NULL;
   const uintptr_t al = (uintptr_t)q_nope | (uintptr_t)q_rope | (uintptr_t)k_nope |
                        (uintptr_t)k_rope | (uintptr_t)v | (uintptr_t)o;

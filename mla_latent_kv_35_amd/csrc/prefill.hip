@@ -152,6 +152,14 @@ void prefill_kernel(PrefillParams p) {
   float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};   // this lane's two queries
   const float sl2 = p.scale_log2;
 
+  //   k_nope: key 16kb + i16, chunk (4ks + G4) ^ i16 -> i16*256 + 16(G4^i16), ^ 64ks
+  //   k_rope: chunk (4ks' + G4) ^ (i16 >> 1) -> i16*128 + 16(G4^(i16>>1)), ^ 64ks'
+  //   V: key rows 32kk + tl and +16, tl = 4G4 + i16/4, bytes 8(i16&3) of dv
+  //      block nb ^ (tl & 7) -> tl*256 + 32(tl&7) + 8(i16&3), ^ 32nb
+  const uint32_t lane_kq = (uint32_t)(i16 * kKRow + 16 * (G4 ^ i16));
+  const uint32_t lane_rq = (uint32_t)(i16 * kRRow + 16 * (G4 ^ (i16 >> 1)));
+  const int v_tl = 4 * G4 + (i16 >> 2);
+  const uint32_t lane_vq = (uint32_t)(v_tl * kKRow + 32 * (v_tl & 7) + 8 * (i16 & 3));
   for (int tile = 0; tile < n_tiles; ++tile) {
     const int t0 = tile * kKTile;
     dma_wait<0>();                               // this wave's copies of tile `tile` landed
@@ -159,8 +167,13 @@ void prefill_kernel(PrefillParams p) {
     if (tile + 1 < n_tiles) issue_tile(tile + 1);
     // keys past the wave's last query are masked for all of its queries
     if (!active || t0 > shift + wq1) continue;
-    const lds_char* const kt = smem + (tile & 1) * kBuf;
-    const lds_char* const vt = kt + kOffV;
+    // fragment addresses: the swizzles XOR bits 4..7 of a row's bytes only,
+    // so a fragment's address is a per-lane base XOR a per-k-step (or per-dv-
+    // block) constant plus an immediate; the bases are made opaque here so
+    // that one register per base is kept instead of one per fragment
+    uint32_t kq = lane_kq + (uint32_t)(tile & 1) * kBuf, rq = lane_rq + (uint32_t)(tile & 1) * kBuf;
+    uint32_t vq = lane_vq + (uint32_t)(tile & 1) * kBuf;
+    asm volatile("" : "+v"(kq), "+v"(rq), "+v"(vq));
     // ---- scores S^T for the 4 key blocks of the tile and both query columns
     // fragment f = (key block f / 6, k-step f % 6); a ring of kRing reads
     // stays in flight ahead of the MFMAs that consume them
@@ -168,9 +181,9 @@ void prefill_kernel(PrefillParams p) {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) s[kb][0] = s[kb][1] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
     auto kfrag = [&](int f) __attribute__((always_inline)) -> bf16x8_t {
-      const int t = 16 * (f / 6) + i16, ks = f % 6;   // this lane's key (A row), k-step
-      return lds_read_b128(ks < 4 ? kt + t * kKRow + 16 * k_pos(t, 4 * ks + G4)
-                                  : kt + kOffKr + t * kRRow + 16 * r_pos(t, 4 * (ks - 4) + G4));
+      const int kb = f / 6, ks = f % 6;
+      return lds_read_b128(ks < 4 ? smem + 16 * kKRow * kb + (kq ^ (64 * ks))
+                                  : smem + kOffKr + 16 * kRRow * kb + (rq ^ (64 * (ks - 4))));
     };
     constexpr int kRing = 6;
     bf16x8_t ring[kRing];
@@ -190,11 +203,8 @@ void prefill_kernel(PrefillParams p) {
     // f = (step f / 8, dv block f % 8), two transposed reads each; the first
     // kVRing are read now, under the softmax, the rest kVRing ahead of use
     auto vfrag = [&](int f) __attribute__((always_inline)) -> bf16x8_t {
-      const int tl = 32 * (f / 8) + 4 * G4 + (i16 >> 2);   // key row this lane addresses
-      const int th = tl + 16;
-      const int byte = 32 * (f % 8) + 8 * (i16 & 3);
-      return concat(lds_read_tr16(vt + tl * kKRow + v_byte(tl, byte)),
-                    lds_read_tr16(vt + th * kKRow + v_byte(th, byte)));
+      const lds_char* const lo = smem + kOffV + 32 * kKRow * (f / 8) + (vq ^ (32 * (f % 8)));
+      return concat(lds_read_tr16(lo), lds_read_tr16(lo + 16 * kKRow));
     };
     constexpr int kVRing = 4;
     bf16x8_t vring[kVRing];
