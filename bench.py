@@ -256,6 +256,22 @@ def main():
                    "mfma_frac_bf16": round(pf_flops / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                    "expand_ms": round(exp_ms, 4)}
 
+    # context: what a plain device-to-device copy reaches on this GPU (read +
+    # write bytes over time; 1 GiB each way, well past the 256 MB Infinity Cache)
+    n_cp = 1 << 30
+    cp_src = torch.ones(n_cp, dtype=torch.uint8, device="cuda")
+    cp_dst = torch.empty_like(cp_src)
+    cp_dst.copy_(cp_src)
+    c0e, c1e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    c0e.record(stream)
+    for _ in range(5):
+        cp_dst.copy_(cp_src)
+    c1e.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * n_cp * 5 / (c0e.elapsed_time(c1e) * 1e-3) / 1e9
+    del cp_src, cp_dst
+
     tokens = cfg.B * cfg.T
     value = tokens * steps / el
     dec_s = dur_ms["decode"] * 1e-3
@@ -284,6 +300,9 @@ def main():
         "eager_ms_per_step": round(el_eager / steps * 1e3, 5),
         "append_ms": round(dur_ms["append"], 5),
         "prefill": prefill,
+        "copy_context": {"what": "torch device-to-device copy of 1 GiB, read + write bytes / time",
+                         "gbps": round(copy_gbps, 1),
+                         "decode_hbm_over_copy": round(achieved / copy_gbps, 4)},
         "launch": "hip graph of %d steps per replay" % per_graph,
         "roofline": {
             "kernel": "mla_decode_paged (split-KV kernel + log-sum-exp combine)",

@@ -44,6 +44,7 @@
 //
 // The split ends by writing either u = U / l and lse, or fp32 partials
 // (m, l, U) for the log-sum-exp combine kernel.
+#include "dma.h"
 #include "mla_device.h"
 #include "mla_internal.h"
 
@@ -119,58 +120,6 @@ __device__ __forceinline__ int swz_p(int r) {
 }
 // Rope rows (128 B): chunk j (0..7) of token t lives at chunk j ^ ((t>>1)&7).
 __device__ __forceinline__ int swz_rope(int t) { return (t >> 1) & 7; }
-
-// Workgroup barrier that orders LDS traffic only: this wave's LDS operations
-// complete (lgkmcnt 0), then all waves meet. In-flight page copies (vmcnt)
-// keep running across it. The memory clobber keeps the compiler from moving
-// memory accesses across the barrier.
-__device__ __forceinline__ void lds_sync() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// Wait until at most N of this wave's page copies are in flight (copies
-// complete in issue order).
-template <int N>
-__device__ __forceinline__ void wait_copies() {
-  static_assert(N >= 0 && N <= 15, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
-}
-
-// One asynchronous 16-byte-per-lane global -> LDS copy: lane i's 16 bytes
-// from page + voff land at LDS byte address lds + 16*i. Written as inline
-// assembly so the compiler's wait insertion never serializes it with later
-// LDS traffic; the issuing wave waits for it explicitly (wait_copies) before
-// the barrier that publishes the tile. It has no output registers, and its
-// address operands are consumed at issue. m0 (the LDS base register of the
-// copy) is restored afterwards.
-__device__ __forceinline__ void dma16(const void* page, uint32_t voff, const lds_char* lds) {
-  const uint32_t lds_addr = (uint32_t)(uintptr_t)lds;
-  uint32_t saved_m0;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %2, %3\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved_m0)
-      : "s"(lds_addr), "v"(voff), "s"(page)
-      : "memory");
-}
-
-// The same as dma16 with 4 bytes per lane (lane i's word lands at lds + 4*i).
-__device__ __forceinline__ void dma4(const void* base, uint32_t voff, const lds_char* lds) {
-  const uint32_t lds_addr = (uint32_t)(uintptr_t)lds;
-  uint32_t saved_m0;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dword %2, %3\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved_m0)
-      : "s"(lds_addr), "v"(voff), "s"(base)
-      : "memory");
-}
 
 // 8 E4M3FN bytes -> 8 bf16 (exact: every E4M3FN value is a bf16 value).
 __device__ __forceinline__ bf16x8_t fp8x8_to_bf16(const i32x2_t& v) {
@@ -307,7 +256,7 @@ void decode_mfma_kernel(DecodeParams p) {
     if (th == 0) q_stage(std::integral_constant<int, 0>{});
     else q_stage(std::integral_constant<int, 1>{});
     if (lane == 0) flags[w] = -1;
-    lds_sync();  // (Q) both halves staged
+    lds_barrier();  // (Q) both halves staged
     if (th == 0) q_half(std::integral_constant<int, 1>{}, true);
     else q_half(std::integral_constant<int, 0>{}, true);
     // visible-token limit of a row: s < min(L - T + t + 1, tok1)
@@ -330,7 +279,7 @@ void decode_mfma_kernel(DecodeParams p) {
     // reach past the group's first row limit need
     auto step = [&](int j, auto masked_c) __attribute__((always_inline)) {
       constexpr bool kMasked = decltype(masked_c)::value;
-      lds_sync();  // (X) tile j resident
+      lds_barrier();  // (X) tile j resident
       f32x4_t S[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
       const int stok0 = tok0 + j * kTileTok;   // first token of tile j
       f32x4_t tsc = {1.f, 1.f, 1.f, 1.f};       // fp8: scales of this lane's 4 tokens
@@ -470,7 +419,7 @@ void decode_mfma_kernel(DecodeParams p) {
         mbuf[32 * hh + 16 + lane] = m_s[1];
       }
     }
-    lds_sync();  // (Z) row sums and reference maxima published
+    lds_barrier();  // (Z) row sums and reference maxima published
     return;
   }
 
@@ -522,22 +471,22 @@ void decode_mfma_kernel(DecodeParams p) {
       if constexpr (!FP8) {
         const int t = 4 * op + v;
         const int ts = min(src.base_t + t, src.last);
-        dma16(src.cp, (uint32_t)(ts * 1024) + lat_off[op & 3], src.tile + t * 1024);
+        dma_copy16(src.cp, (uint32_t)(ts * 1024) + lat_off[op & 3], src.tile + t * 1024);
       } else {
         const int q = 4 * op + v;                   // rows 2q (lanes 0-31), 2q+1 (32-63)
         const int t = 2 * q + (lane >> 5);
         const int ts = min(src.base_t + t, src.last);
         const int jc = (lane & 31) ^ (t & 15);      // 16-B chunk of the 512-B row
-        dma16(src.cp, (uint32_t)(ts * 512 + jc * 16), src.tile + 2 * q * 512);
+        dma_copy16(src.cp, (uint32_t)(ts * 512 + jc * 16), src.tile + 2 * q * 512);
       }
     } else if (op == (FP8 ? 4 : 8)) {
       const int t = 8 * v + (lane >> 3);
       const int ts = min(src.base_t + t, src.last);
       const int jc = (lane & 7) ^ swz_rope(t);
-      dma16(src.rp, (uint32_t)(ts * 128 + jc * 16), src.tile + kLatTile + v * 1024);
+      dma_copy16(src.rp, (uint32_t)(ts * 128 + jc * 16), src.tile + kLatTile + v * 1024);
     } else if constexpr (FP8) {
       const int ts = min(src.base_t + (lane & 31), src.last);
-      dma4(src.sp, (uint32_t)(ts * 4), src.tile + Gm::kScaleOff);
+      dma_copy4(src.sp, (uint32_t)(ts * 4), src.tile + Gm::kScaleOff);
     }
   };
   auto issue_tile = [&](int jt) __attribute__((always_inline)) {
@@ -549,10 +498,10 @@ void decode_mfma_kernel(DecodeParams p) {
   // this wave's copies of one tile must have landed: at most `pending` of the
   // next tile's copies may still be in flight
   auto wait_tile = [&](bool pending) __attribute__((always_inline)) {
-    if (!pending) wait_copies<0>();
-    else if (!FP8) wait_copies<9>();
-    else if (v == 0) wait_copies<6>();
-    else wait_copies<5>();
+    if (!pending) dma_wait<0>();
+    else if (!FP8) dma_wait<9>();
+    else if (v == 0) dma_wait<6>();
+    else dma_wait<5>();
   };
 
   f32x4_t U[4][8];
@@ -565,7 +514,7 @@ void decode_mfma_kernel(DecodeParams p) {
 
   issue_tile(0);
   if (n_tiles > 1) issue_tile(1);
-  lds_sync();  // (Q) the score team's queries staged; the copies fly on
+  lds_barrier();  // (Q) the score team's queries staged; the copies fly on
   wait_tile(n_tiles > 1);
 
   bf16x8_t pa[4];
@@ -623,7 +572,7 @@ void decode_mfma_kernel(DecodeParams p) {
   };
 
   for (int j = 0; j <= n_tiles; ++j) {
-    lds_sync();  // (X) tile j resident; P(j-1) and alpha(j-1) published
+    lds_barrier();  // (X) tile j resident; P(j-1) and alpha(j-1) published
     const bool more = j + 2 < n_tiles;
     const TileSrc src = tile_src(more ? j + 2 : 0);
     if (more && j == 0) issue_tile(j + 2);
@@ -660,7 +609,7 @@ void decode_mfma_kernel(DecodeParams p) {
     // tile j+1 must be resident at the next (X); tile j+2's copies may fly on
     wait_tile(more);
   }
-  lds_sync();  // (Z) row sums and reference maxima published
+  lds_barrier();  // (Z) row sums and reference maxima published
 
   // ---- finish: u = U / l or fp32 partials ----------------------------------
 #pragma unroll

@@ -64,14 +64,6 @@ __device__ __forceinline__ bf16x8_t load_bf16x8(const uint16_t* p) {
   return *(const bf16x8_t*)p;
 }
 
-// Asynchronous 16-byte global -> LDS copy: lane i's 16 bytes land at
-// dst + 16*i (dst is wave-uniform). Completion is tracked by vmcnt.
-__device__ __forceinline__ void global_to_lds16(const void* src, lds_char* dst) {
-  __builtin_amdgcn_global_load_lds(src, (MLA_LDS void*)dst, 16, 0, 0);
-}
-
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70 & 0xc07f); }
-
 // 2^x on the hardware transcendental unit (results below 2^-126 flush to 0,
 // which is immaterial for softmax weights next to the row maximum's 2^0).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -75,6 +75,7 @@ def run_prefill(mla, c, kr, wk, wv, qn, qr, scale, out_dtype=torch.bfloat16):
     (1, 32, 130, 2, None),        # two speculative tokens
     (3, 16, 64, 1, None),         # one query, exactly one key tile
     (1, 128, 1000, 1000, 24),     # larger: sampled query rows
+    (1, 128, 4096, 4096, 6),      # the benchmarked shape: sampled query rows
 ])
 def test_prefill_parity(mla, B, H, n_kv, n_q, sample):
     rng = np.random.default_rng(B * 1000 + n_kv + n_q)
