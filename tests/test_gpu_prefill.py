@@ -100,6 +100,26 @@ def test_prefill_parity(mla, B, H, n_kv, n_q, sample):
         assert np.abs(lse[b][rows].reshape(-1) - (m + np.log(l))).max() <= 5e-2
 
 
+@pytest.mark.parametrize("B,H,n_kv,n_q", [
+    (1, 20, 333, 333),            # B*H not a multiple of 8: plain workgroup order
+    (3, 4, 70, 70),               # 12 heads in all, one query block each, ragged key tile
+])
+def test_prefill_parity_f32_output_odd_heads(mla, B, H, n_kv, n_q):
+    rng = np.random.default_rng(B * 77 + H)
+    c, kr, wk, wv = make_prefill(rng, B, H, n_kv)
+    qn = synth.store(rng.standard_normal((B, n_q, H, 128)), "bf16")
+    qr = synth.store(rng.standard_normal((B, n_q, H, 64)), "bf16")
+    scale = 192 ** -0.5
+    o, lse = run_prefill(mla, c, kr, wk, wv, qn, qr, scale, out_dtype=torch.float32)
+    Wk, Wv = O.stored_to_f64(wk, "bf16"), O.stored_to_f64(wv, "bf16")
+    for b in range(B):
+        C, KR = O.stored_to_f64(c[b], "bf16"), O.stored_to_f64(kr[b], "bf16")
+        QN, QR = O.stored_to_f64(qn[b], "bf16"), O.stored_to_f64(qr[b], "bf16")
+        visible = n_kv - n_q + np.arange(n_q) + 1
+        ref, _ = O.explicit_mha(QN, QR, C, KR, Wk, Wv, scale, visible)
+        assert row_rel(o[b], ref) <= 2e-2
+
+
 @pytest.mark.parametrize("T", [1, 2])
 def test_explicit_prefill_equals_absorbed_decode(mla, T):
     """Section 6.1's check: the same queries and cache through both forms."""
