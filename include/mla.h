@@ -69,7 +69,8 @@ int mla_abi_version(void);
  *   q_nope : [n_tok][H][d_h]  dtype q_dt (F32 or BF16)
  *   w_uk   : [H][d_h][d_c]    dtype q_dt (head h's up-projection, d_h x d_c)
  *   q_lat  : [n_tok][H][d_c]  dtype out_dt (F32, or BF16 when q_dt is BF16)
- * Supported: d_h = 128, d_c = 512, n_tok >= 0 (0 launches nothing), H >= 1.
+ * Supported: d_h = 128, d_c = 512, n_tok >= 0 (0 launches nothing), H >= 1,
+ * 16-byte aligned tensors (else MLA_ERR_UNSUPPORTED).
  * Accumulation is fp32; F32 inputs use fp32 FMA end to end.
  */
 int mla_absorb_q(const void* q_nope, const void* w_uk, void* q_lat,
@@ -239,7 +240,8 @@ int mla_decode_paged(const mla_decode_args* args, void* stream);
  *   u    : [n_tok][H][d_c]  dtype u_dt (F32 or BF16)
  *   w_uv : [H][d_h][d_c]    dtype w_dt (F32 or BF16; F32 requires u_dt F32)
  *   o    : [n_tok][H][d_h]  dtype o_dt (F32 or BF16)
- * Supported: d_h = 128, d_c = 512. fp32 accumulation.
+ * Supported: d_h = 128, d_c = 512, 16-byte aligned tensors (else
+ * MLA_ERR_UNSUPPORTED). fp32 accumulation.
  */
 int mla_out_proj(const void* u, const void* w_uv, void* o, int u_dt, int w_dt,
                  int o_dt, int n_tok, int H, int d_h, int d_c, void* stream);
@@ -311,7 +313,8 @@ int mla_cache_append(const mla_append_args* args, void* stream);
  *   c            : [n_tok][d_c]     dtype c_dt (F32 or BF16), the latents
  *   w_uk, w_uv   : [H][d_h][d_c]    dtype w_dt (BF16, or F32 with F32 c and outputs)
  *   k_nope, v    : [n_tok][H][d_h]  dtype out_dt (F32 or BF16)
- * Supported: d_h = 128, d_c = 512; fp32 accumulation (as mla_out_proj).
+ * Supported: d_h = 128, d_c = 512, 16-byte aligned tensors (else
+ * MLA_ERR_UNSUPPORTED); fp32 accumulation (as mla_out_proj).
  */
 int mla_expand_kv(const void* c, const void* w_uk, const void* w_uv, void* k_nope, void* v,
                   int c_dt, int w_dt, int out_dt, int n_tok, int H, int d_h, int d_c,

@@ -132,21 +132,34 @@ __global__ __launch_bounds__(kThreads) void absorb_rope_kernel(
   }
 }
 
+// fp32: one workgroup of 4 waves per (token, head, 256 latent dims); wave w
+// sums head dims j = 32w..32w+31 for every dim d = thread (coalesced rows of
+// W_UK[h]), then the four partial sums are added in a fixed order.
+constexpr int kF32Dims = 256;
+
 __global__ __launch_bounds__(kThreads) void absorb_f32_kernel(const float* __restrict__ q,
                                                               const float* __restrict__ wuk,
                                                               float* __restrict__ out, int n_tok,
                                                               int H) {
-  __shared__ float qs[kDh];
+  __shared__ float part[kThreads / 64][kF32Dims];
   const int nh = blockIdx.x;          // n*H + h
   const int h = nh % H;
-  if (threadIdx.x < kDh) qs[threadIdx.x] = q[(size_t)nh * kDh + threadIdx.x];
-  __syncthreads();
-  const float* wh = wuk + (size_t)h * kDh * kDc;
-  for (int d = threadIdx.x; d < kDc; d += kThreads) {
-    float acc = 0.f;
-    for (int j = 0; j < kDh; ++j) acc = fmaf(qs[j], wh[(size_t)j * kDc + d], acc);
-    out[(size_t)nh * kDc + d] = acc;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int d0 = blockIdx.y * kF32Dims;
+  const float* qr = q + (size_t)nh * kDh + 32 * w;
+  const float* wh = wuk + ((size_t)h * kDh + 32 * w) * kDc + d0;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+  for (int j = 0; j < 32; ++j) {
+    const float qj = qr[j];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = fmaf(qj, wh[(size_t)j * kDc + lane + 64 * i], acc[i]);
   }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) part[w][lane + 64 * i] = acc[i];
+  __syncthreads();
+  const int d = threadIdx.x;
+  out[(size_t)nh * kDc + d0 + d] = ((part[0][d] + part[1][d]) + part[2][d]) + part[3][d];
 }
 
 }  // namespace
@@ -164,7 +177,7 @@ hipError_t launch_absorb(const void* q_nope, const void* w_uk, void* q_lat, int 
       hipLaunchKernelGGL(absorb_bf16_kernel<false>, grid, dim3(kThreads), 0, s,
                          (const uint16_t*)q_nope, (const uint16_t*)w_uk, q_lat, n_tok, H, n_tb);
   } else {
-    hipLaunchKernelGGL(absorb_f32_kernel, dim3(n_tok * H), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL(absorb_f32_kernel, dim3(n_tok * H, kDc / kF32Dims), dim3(kThreads), 0, s,
                        (const float*)q_nope, (const float*)w_uk, (float*)q_lat, n_tok, H);
   }
   return hipGetLastError();

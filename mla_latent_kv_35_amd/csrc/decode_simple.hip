@@ -1,13 +1,16 @@
 // Paged absorbed-MLA decode for fp32 caches, fp32 arithmetic end to end.
 //
-// One workgroup per (sequence b, split k, query row r). Tokens of the split
-// are taken 256 at a time: each thread forms one token's score
+// One workgroup of 4 waves per (sequence b, split k, query row r). The
+// split's tokens go to the waves in batches of kBatch (wave w takes batches
+// w, w + 4, ...). For each token a wave reads the cached row coalesced (lane i
+// holds latent values 8i..8i+7 and rope value i), forms the score
 // z = (q_lat . c_s + q_rope . k^R_s) * scale (PaperTrace "02 · DeepSeek-V2
-// analysis", eq. 18 over the 576 cached elements) in fp32 FMA, the chunk's
-// max and exponentials update an online softmax, and each thread accumulates
-// two latent dimensions of u = sum_s a_s c_s (section 6.1) over the chunk's
-// tokens in increasing token order. Reductions use a fixed tree, so results
-// are deterministic.
+// analysis", eq. 18 over the 576 cached elements) by a fixed butterfly sum,
+// and folds it into the wave's online softmax; the latent aggregate
+// u = sum_s a_s c_s (section 6.1) reuses the row already in registers. The
+// four waves' (max, sum, aggregate) are merged by log-sum-exp in a fixed
+// order, so results are deterministic. All loads of a batch are issued
+// before any of them is used.
 #include "mla_device.h"
 #include "mla_internal.h"
 
@@ -15,32 +18,24 @@ namespace mla {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kBatch = 8;
 
-__device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) {
-  for (int off = 32; off > 0; off >>= 1) {
-    const float o = __shfl_xor(v, off);
-    v = is_max ? fmaxf(v, o) : v + o;
-  }
-  const int tid = threadIdx.x;
-  __syncthreads();
-  if ((tid & 63) == 0) red[tid >> 6] = v;
-  __syncthreads();
-  float r = red[0];
-  for (int i = 1; i < kThreads / 64; ++i) r = is_max ? fmaxf(r, red[i]) : r + red[i];
-  return r;
+__device__ __forceinline__ float wave_sum_all(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  return v;
 }
 
 __global__ __launch_bounds__(kThreads) void decode_simple_f32_kernel(DecodeParams p) {
-  __shared__ float q[kDc + kDr];
-  __shared__ float pr[kThreads];
-  __shared__ int tokpage[kThreads];
-  __shared__ float red[kThreads / 64];
+  __shared__ float wm[kWaves], wl[kWaves];
+  __shared__ __attribute__((aligned(16))) float wu[kWaves][kDc];
 
   const int r = blockIdx.x % p.R;
   const int bk = blockIdx.x / p.R;
   const int k = bk % p.n_split;
   const int b = bk / p.n_split;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
 
   const int L = p.seq_lens[b];
   bool bad = (L < p.T) || (L > p.max_seq_len) || ((L + kPage - 1) / kPage > p.max_pages);
@@ -59,65 +54,95 @@ __global__ __launch_bounds__(kThreads) void decode_simple_f32_kernel(DecodeParam
     bad = __syncthreads_or(lb);
   }
 
-  float m = -INFINITY, l = 0.f, u0 = 0.f, u1 = 0.f;
-  if (bad) {
-    m = l = u0 = u1 = __builtin_nanf("");
-  } else {
-    const float* ql = (const float*)p.q_lat + ((size_t)b * p.R + r) * kDc;
-    const float* qr = (const float*)p.q_rope + ((size_t)b * p.R + r) * kDr;
-    for (int i = tid; i < kDc; i += kThreads) q[i] = ql[i];
-    if (tid < kDr) q[kDc + tid] = qr[tid];
-    __syncthreads();
+  float m = -INFINITY, l = 0.f, u[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) u[i] = 0.f;
+  if (!bad) {
+    const float* qrow = (const float*)p.q_lat + ((size_t)b * p.R + r) * kDc + 8 * lane;
+    const f32x4_t q0 = *(const f32x4_t*)qrow, q1 = *(const f32x4_t*)(qrow + 4);
+    const float qr = ((const float*)p.q_rope)[((size_t)b * p.R + r) * kDr + lane];
     const float* ckv = (const float*)p.ckv;
     const float* kr = (const float*)p.kr;
-    for (int c0 = tok0; c0 < lim; c0 += kThreads) {
-      const int s = c0 + tid;
-      float z = -INFINITY;
-      int page = 0;
-      if (s < lim) {
-        page = btrow[s / kPage];
-        const float* cs = ckv + ((size_t)page * kPage + s % kPage) * kDc;
-        const float* ks = kr + ((size_t)page * kPage + s % kPage) * kDr;
-        float acc = 0.f;
-        for (int d = 0; d < kDc; ++d) acc = fmaf(q[d], cs[d], acc);
-        float accr = 0.f;
-        for (int d = 0; d < kDr; ++d) accr = fmaf(q[kDc + d], ks[d], accr);
-        z = (acc + accr) * p.scale_log2;
+    for (int c0 = tok0 + kBatch * w; c0 < lim; c0 += kBatch * kWaves) {
+      f32x4_t c[kBatch][2];
+      float cr[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int s = min(c0 + j, lim - 1);   // past the limit: reread the last row, masked below
+        const size_t row = (size_t)btrow[s / kPage] * kPage + s % kPage;
+        c[j][0] = *(const f32x4_t*)(ckv + row * kDc + 8 * lane);
+        c[j][1] = *(const f32x4_t*)(ckv + row * kDc + 8 * lane + 4);
+        cr[j] = kr[row * kDr + lane];
       }
-      const float cmax = block_reduce(z, red, true);
-      const float mnew = fmaxf(m, cmax);
-      const float alpha = exp2f(m - mnew);   // m = -inf on the first chunk -> 0
-      const float e = (s < lim) ? exp2f(z - mnew) : 0.f;
-      pr[tid] = e;
-      tokpage[tid] = page;
-      const float esum = block_reduce(e, red, false);  // syncs: pr visible
-      l = l * alpha + esum;
-      u0 *= alpha;
-      u1 *= alpha;
-      const int n = min(kThreads, lim - c0);
-      for (int j = 0; j < n; ++j) {
-        const int sj = c0 + j;
-        const float* cs = ckv + ((size_t)tokpage[j] * kPage + sj % kPage) * kDc;
-        u0 = fmaf(pr[j], cs[tid], u0);
-        u1 = fmaf(pr[j], cs[tid + kThreads], u1);
+      float z[kBatch];
+      float mt = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        float acc = qr * cr[j];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc = fmaf(q0[i], c[j][0][i], acc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc = fmaf(q1[i], c[j][1][i], acc);
+        z[j] = (c0 + j < lim) ? wave_sum_all(acc) * p.scale_log2 : -INFINITY;
+        mt = fmaxf(mt, z[j]);
+      }
+      const float mnew = fmaxf(m, mt);                   // finite: token c0 is visible
+      const float alpha = exp2f(m - mnew);               // m = -inf on the first batch -> 0
+      l *= alpha;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) u[i] *= alpha;
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const float e = exp2f(z[j] - mnew);              // 0 past the limit
+        l += e;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          u[i] = fmaf(e, c[j][0][i], u[i]);
+          u[4 + i] = fmaf(e, c[j][1][i], u[4 + i]);
+        }
       }
       m = mnew;
-      __syncthreads();
     }
   }
+  // merge the waves: M = max m_w, weights 2^(m_w - M) (0 for a wave that saw no token)
+  if (lane == 0) {
+    wm[w] = m;
+    wl[w] = l;
+  }
+  *(f32x4_t*)&wu[w][8 * lane] = (f32x4_t){u[0], u[1], u[2], u[3]};
+  *(f32x4_t*)&wu[w][8 * lane + 4] = (f32x4_t){u[4], u[5], u[6], u[7]};
+  __syncthreads();
+  float M = wm[0];
+#pragma unroll
+  for (int i = 1; i < kWaves; ++i) M = fmaxf(M, wm[i]);
+  float cw[kWaves], lsum = 0.f;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    cw[i] = (wm[i] == -INFINITY) ? 0.f : exp2f(wm[i] - M);
+    lsum = fmaf(cw[i], wl[i], lsum);
+  }
+  float U[2];
+#pragma unroll
+  for (int d = 0; d < 2; ++d) {
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) acc = fmaf(cw[i], wu[i][tid + d * kThreads], acc);
+    U[d] = acc;
+  }
+  if (bad) M = lsum = U[0] = U[1] = __builtin_nanf("");
 
   if (p.n_split == 1) {
     const size_t o = ((size_t)b * p.R + r) * kDc;
-    ((float*)p.out)[o + tid] = u0 / l;
-    ((float*)p.out)[o + tid + kThreads] = u1 / l;
-    if (p.lse && tid == 0) p.lse[(size_t)b * p.R + r] = (m + log2f(l)) * kLn2;
+    ((float*)p.out)[o + tid] = U[0] / lsum;
+    ((float*)p.out)[o + tid + kThreads] = U[1] / lsum;
+    if (p.lse && tid == 0) p.lse[(size_t)b * p.R + r] = (M + log2f(lsum)) * kLn2;
   } else {
     const size_t base = ((size_t)b * p.n_split + k) * p.R + r;
-    p.part_u[base * kDc + tid] = u0;
-    p.part_u[base * kDc + tid + kThreads] = u1;
+    p.part_u[base * kDc + tid] = U[0];
+    p.part_u[base * kDc + tid + kThreads] = U[1];
     if (tid == 0) {
-      p.part_ml[base * 2] = m;
-      p.part_ml[base * 2 + 1] = l;
+      p.part_ml[base * 2] = M;
+      p.part_ml[base * 2 + 1] = lsum;
     }
   }
 }

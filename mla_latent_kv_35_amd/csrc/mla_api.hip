@@ -118,6 +118,7 @@ int mla_absorb_q(const void* q_nope, const void* w_uk, void* q_lat, int q_dt, in
   if (q_dt == MLA_F32 && out_dt != MLA_F32) return MLA_ERR_DTYPE;
   if (n_tok == 0) return MLA_OK;
   if (!q_nope || !w_uk || !q_lat) return MLA_ERR_NULL;
+  if ((((uintptr_t)q_nope | (uintptr_t)w_uk | (uintptr_t)q_lat) & 15) != 0) return MLA_ERR_UNSUPPORTED;
   const hipError_t e = launch_absorb(q_nope, w_uk, q_lat, q_dt == MLA_BF16, out_dt == MLA_BF16,
                                      n_tok, H, (hipStream_t)stream);
   return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
@@ -160,6 +161,7 @@ int mla_absorb_q_rope(const void* q_nope, const void* w_uk, void* q_lat, int q_d
   if (!theta && (!(base > 0.0) || !isfinite(base))) return MLA_ERR_SHAPE;
   if (n_tok == 0) return MLA_OK;
   if (!q_nope || !w_uk || !q_lat || !q_rope || !q_rot || !pos) return MLA_ERR_NULL;
+  if ((((uintptr_t)q_nope | (uintptr_t)w_uk | (uintptr_t)q_lat) & 15) != 0) return MLA_ERR_UNSUPPORTED;
   const hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if (q_dt == MLA_BF16 && rope_dt == MLA_BF16 && d_r == 64 &&
@@ -305,6 +307,7 @@ int mla_out_proj(const void* u, const void* w_uv, void* o, int u_dt, int w_dt, i
   if (w_dt == MLA_F32 && (u_dt != MLA_F32 || o_dt != MLA_F32)) return MLA_ERR_DTYPE;
   if (n_tok == 0) return MLA_OK;
   if (!u || !w_uv || !o) return MLA_ERR_NULL;
+  if ((((uintptr_t)u | (uintptr_t)w_uv | (uintptr_t)o) & 15) != 0) return MLA_ERR_UNSUPPORTED;
   const hipError_t e = launch_out_proj(u, w_uv, o, u_dt == MLA_BF16, w_dt == MLA_BF16,
                                        o_dt == MLA_BF16, n_tok, H, (hipStream_t)stream);
   return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
@@ -319,6 +322,8 @@ int mla_expand_kv(const void* c, const void* w_uk, const void* w_uv, void* k_nop
   if (w_dt == MLA_F32 && (c_dt != MLA_F32 || out_dt != MLA_F32)) return MLA_ERR_DTYPE;
   if (n_tok == 0) return MLA_OK;
   if (!c || !w_uk || !w_uv || !k_nope || !v) return MLA_ERR_NULL;
+  if ((((uintptr_t)c | (uintptr_t)w_uk | (uintptr_t)w_uv | (uintptr_t)k_nope | (uintptr_t)v) & 15) != 0)
+    return MLA_ERR_UNSUPPORTED;
   const hipStream_t s = (hipStream_t)stream;
   for (int i = 0; i < 2; ++i) {
     const void* w = i == 0 ? w_uk : w_uv;

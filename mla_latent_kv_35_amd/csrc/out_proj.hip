@@ -86,21 +86,42 @@ __global__ __launch_bounds__(kThreads) void out_proj_bf16_kernel(const void* __r
     }
 }
 
-__global__ __launch_bounds__(kDh) void out_proj_f32_kernel(const float* __restrict__ u,
-                                                          const float* __restrict__ wuv,
-                                                          float* __restrict__ o, int H, long u_tok,
-                                                          long u_head) {
-  __shared__ float us[kDc];
+// fp32: one workgroup of 4 waves per (token, head, 32 outputs); wave w
+// produces 8 outputs. Lane i holds u values 8i..8i+7; each output row
+// W_UV[h][j] is read coalesced (8 values per lane), the wave's 8 rows all in
+// flight at once, and summed by a fixed butterfly.
+constexpr int kF32Waves = 4;
+constexpr int kF32Rows = 8;                                  // outputs per wave
+constexpr int kF32Blocks = kDh / (kF32Waves * kF32Rows);     // workgroups per (token, head)
+
+__global__ __launch_bounds__(64 * kF32Waves) void out_proj_f32_kernel(const float* __restrict__ u,
+                                                                    const float* __restrict__ wuv,
+                                                                    float* __restrict__ o, int H,
+                                                                    long u_tok, long u_head) {
   const int nh = blockIdx.x;
   const int h = nh % H;
-  const float* ur = u + (size_t)(nh / H) * u_tok + (size_t)h * u_head;
-  for (int d = threadIdx.x; d < kDc; d += kDh) us[d] = ur[d];
-  __syncthreads();
-  const int j = threadIdx.x;
-  const float* wr = wuv + ((size_t)h * kDh + j) * kDc;
-  float acc = 0.f;
-  for (int d = 0; d < kDc; ++d) acc = fmaf(wr[d], us[d], acc);
-  o[(size_t)nh * kDh + j] = acc;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int j0 = (blockIdx.y * kF32Waves + w) * kF32Rows;     // first output of this wave
+  const float* ur = u + (size_t)(nh / H) * u_tok + (size_t)h * u_head + 8 * lane;
+  f32x4_t wa[kF32Rows], wb[kF32Rows];
+#pragma unroll
+  for (int jj = 0; jj < kF32Rows; ++jj) {
+    const float* wr = wuv + ((size_t)h * kDh + j0 + jj) * kDc + 8 * lane;
+    wa[jj] = *(const f32x4_t*)wr;
+    wb[jj] = *(const f32x4_t*)(wr + 4);
+  }
+  const f32x4_t u0 = *(const f32x4_t*)ur, u1 = *(const f32x4_t*)(ur + 4);
+#pragma unroll
+  for (int jj = 0; jj < kF32Rows; ++jj) {
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc = fmaf(wa[jj][i], u0[i], acc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc = fmaf(wb[jj][i], u1[i], acc);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    if (lane == 0) o[(size_t)nh * kDh + j0 + jj] = acc;
+  }
 }
 
 }  // namespace
@@ -132,8 +153,8 @@ hipError_t launch_out_proj_strided(const void* u, long u_tok, long u_head, const
       hipLaunchKernelGGL((out_proj_bf16_kernel<false, false>), grid, dim3(kThreads), 0, s, u, w, o, n_tok, H, n_tb,
                          u_tok, u_head);
   } else {
-    hipLaunchKernelGGL(out_proj_f32_kernel, dim3(n_tok * H), dim3(kDh), 0, s, (const float*)u,
-                       (const float*)w_uv, (float*)o, H, u_tok, u_head);
+    hipLaunchKernelGGL(out_proj_f32_kernel, dim3(n_tok * H, kF32Blocks), dim3(64 * kF32Waves), 0, s,
+                       (const float*)u, (const float*)w_uv, (float*)o, H, u_tok, u_head);
   }
   return hipGetLastError();
 }

@@ -175,3 +175,14 @@ def test_absorb_q_rope_rejects_before_launch(B):
     assert f(None, None, None, 1, 1, None, None, 1, None, 4, 128, 128, 512, 64, -1., None, None) == 2
     assert f(None, None, None, 1, 1, None, None, 1, None, -1, 128, 128, 512, 64, 1e4, None, None) == 2
     assert f(None, None, None, 1, 1, None, None, 1, None, 0, 128, 128, 512, 64, 1e4, None, None) == 0
+
+
+def test_dense_entry_points_reject_misaligned_pointers(B):
+    L = B.lib()
+    fake = ctypes.c_void_p(1 << 20)
+    odd = ctypes.c_void_p((1 << 20) + 4)
+    assert L.mla_absorb_q(odd, fake, fake, 0, 0, 4, 8, 128, 512, None) == 4
+    assert L.mla_out_proj(fake, odd, fake, 0, 0, 0, 4, 8, 128, 512, None) == 4
+    assert L.mla_expand_kv(fake, fake, fake, fake, odd, 0, 0, 0, 4, 8, 128, 512, None) == 4
+    assert L.mla_absorb_q_rope(fake, fake, odd, 1, 1, fake, fake, 1, fake, 4, 8, 128, 512, 64,
+                               1e4, None, None) == 4
