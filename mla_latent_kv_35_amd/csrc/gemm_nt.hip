@@ -8,7 +8,8 @@
 // chunks of 32 (one MFMA k-step), double-buffered: the next chunk's global
 // loads are in flight while the current one is multiplied. LDS rows are
 // 80 B apart (64 B of data + 16 B), so the 16 rows of an operand fragment
-// start on 16 different bank quadruples.
+// start on 16 different bank quadruples. The C tile leaves through LDS in
+// whole 256-byte row segments.
 #include "mla_device.h"
 #include "mla_extra.h"
 
@@ -17,7 +18,7 @@ namespace {
 
 constexpr int kTile = 128;
 constexpr int kKc = 32;
-constexpr int kPitch = 80;                         // bytes per LDS row
+constexpr int kPitch = 80;                         // bytes per LDS row: 64 B of data + 16 B
 constexpr int kBuf = kTile * kPitch;               // one operand chunk: 10 KB
 
 template <bool A_BF16, bool C_BF16>
@@ -83,33 +84,59 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(const void* __restrict__ A
   for (int kc = 0; kc < nk; ++kc) {
     const int cur = kc & 1;
     if (kc + 1 < nk) load((kc + 1) * kKc);
-    bf16x8_t a[4], b[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      a[i] = lds_read_b128(smem + cur * kBuf + (64 * wm + 16 * i + i16) * kPitch + 16 * G4);
-      b[i] = lds_read_b128(smem + (2 + cur) * kBuf + (64 * wn + 16 * i + i16) * kPitch + 16 * G4);
+    for (int ks = 0; ks < kKc / 32; ++ks) {
+      bf16x8_t a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[i] = lds_read_b128(smem + cur * kBuf + (64 * wm + 16 * i + i16) * kPitch + 64 * ks + 16 * G4);
+        b[i] = lds_read_b128(smem + (2 + cur) * kBuf + (64 * wn + 16 * i + i16) * kPitch + 64 * ks +
+                             16 * G4);
+      }
+      // B fragments as the MFMA's A operand: the block holds C^T, so a lane
+      // ends with 4 consecutive columns of one row of C
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(b[j], a[i], acc[i][j]);
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(a[i], b[j], acc[i][j]);
     if (kc + 1 < nk) store(cur ^ 1);            // the other buffer was last read one chunk ago
     __syncthreads();
   }
-  // lane holds C[64wm + 16i + 4*G4 + r][64wn + 16j + i16]
+  // lane holds C[64wm + 16i + i16][64wn + 16j + 4*G4 + r], r = 0..3
+  if constexpr (C_BF16) {
+    // stage the bf16 tile in LDS (rows of 256 B + 16 B), then write whole
+    // 256-byte row segments with 16-byte stores; the K loop's last barrier
+    // freed the operand buffers
+    constexpr int kCPitch = kTile * 2 + 16;
+    static_assert(kTile * kCPitch <= 4 * kBuf, "C tile fits in the operand buffers");
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = m0 + 64 * wm + 16 * i + 4 * G4 + r;
+      for (int j = 0; j < 4; ++j)
+        *(MLA_LDS u32x2_t*)(smem + (64 * wm + 16 * i + i16) * kCPitch +
+                            2 * (64 * wn + 16 * j + 4 * G4)) =
+            (u32x2_t){pack_bf16x2(acc[i][j][0], acc[i][j][1]),
+                      pack_bf16x2(acc[i][j][2], acc[i][j][3])};
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < kTile * kTile * 2 / 16 / 256; ++q) {
+      const int e = tid + 256 * q, row = e >> 4, ch = e & 15;
+      const int m = m0 + row;
+      if (m < M)
+        *(u32x4_t*)((uint16_t*)C + (size_t)m * N + n0 + 8 * ch) =
+            *(const MLA_LDS u32x4_t*)(smem + row * kCPitch + 16 * ch);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + 64 * wm + 16 * i + i16;
       if (m >= M) continue;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const size_t off = (size_t)m * N + n0 + 64 * wn + 16 * j + i16;
-        if (C_BF16) ((uint16_t*)C)[off] = f2bf(acc[i][j][r]);
-        else ((float*)C)[off] = acc[i][j][r];
-      }
+      for (int j = 0; j < 4; ++j)
+        *(f32x4_t*)((float*)C + (size_t)m * N + n0 + 64 * wn + 16 * j + 4 * G4) = acc[i][j];
     }
+  }
 }
 
 }  // namespace
