@@ -1,7 +1,7 @@
 """Python binding of libmla.so (ctypes). Argument marshalling only.
 
-Every step of the decode path runs in the HIP kernels behind the C ABI
-declared in include/mla.h; this module allocates outputs and workspaces as
+Every step of the path runs in the HIP kernels behind the C ABI declared in
+include/mla.h; this module allocates outputs and workspaces as
 torch device tensors, passes raw pointers and the current HIP stream, and
 turns non-zero status codes into exceptions. Importing it fails loudly when
 the library has not been built.
@@ -149,7 +149,7 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
 
 
 # ---------------------------------------------------------------------------
-# the four entry points
+# entry points (one function per C call)
 # ---------------------------------------------------------------------------
 
 def absorb_q(q_nope: torch.Tensor, w_uk: torch.Tensor, out_dtype=None,
