@@ -312,6 +312,8 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBPS, 4),
             "traffic": traffic,
+            # the counted HBM bytes (cache, queries, split partials) over the same time
+            "traffic_gbps": None if traffic is None else round(traffic / dec_s / 1e9, 1),
             "algorithmic_bytes_per_launch": cache_bytes,
             "mfma_tflops": round(flops / dec_s / 1e12, 1),
             "mfma_frac_bf16": round(flops / dec_s / 1e12 / PEAK_BF16_TFLOPS, 4),
