@@ -104,18 +104,19 @@ __device__ __forceinline__ float wave_sum64(float v) {
 // Merge of NR rows by one wave: lane i returns u for latent values 8i..8i+7
 // of each row (NaN for a sequence whose length or page count is out of
 // range) and each row's lse. The rows must be wave-uniform. Every load of
-// the first 8 splits (their (m, l) and U, from slots clamped to the
-// allocated n_split) is issued before the sequence length is known, so one
-// memory round trip serves all NR rows; splits past the live count are then
-// masked out and never accumulated.
-template <int NR>
+// the first Q splits (their (m, l) and U, from slots clamped to the
+// allocated n_split; Q = 4 when no more are allocated) is issued before the
+// sequence length is known, so one memory round trip serves all NR rows;
+// splits past the live count are then masked out and never accumulated. The
+// sum runs over k in increasing order whatever Q is.
+template <int NR, int Q = 8>
 __device__ __forceinline__ void combine_rows(const CombineParams& p, const int (&row)[NR], int lane,
                                              float (&u)[NR][8], float (&lse_out)[NR]) {
   const int nsp = p.n_split;                                   // split stride in memory
   const size_t kstride = (size_t)p.R * kDc;
   int Ls[NR];
   float mk[NR], lk[NR];
-  f32x4_t v0[NR][8], v1[NR][8];
+  f32x4_t v0[NR][Q], v1[NR][Q];
   const float* pu[NR];
 #pragma unroll
   for (int t = 0; t < NR; ++t) {
@@ -126,7 +127,7 @@ __device__ __forceinline__ void combine_rows(const CombineParams& p, const int (
     lk[t] = ml[1];
     pu[t] = p.part_u + (((size_t)b * nsp) * p.R + r) * kDc + 8 * lane;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < Q; ++q) {
       const size_t off = (size_t)min(q, nsp - 1) * kstride;
       v0[t][q] = *(const f32x4_t*)(pu[t] + off);
       v1[t][q] = *(const f32x4_t*)(pu[t] + off + 4);
@@ -154,7 +155,7 @@ __device__ __forceinline__ void combine_rows(const CombineParams& p, const int (
     f32x4_t acc0 = w0 * v0[t][0];
     f32x4_t acc1 = w0 * v1[t][0];
 #pragma unroll
-    for (int q = 1; q < 8; ++q) {
+    for (int q = 1; q < Q; ++q) {
       if (q < ns) {
         const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk), q));
 #pragma unroll
@@ -164,7 +165,7 @@ __device__ __forceinline__ void combine_rows(const CombineParams& p, const int (
         }
       }
     }
-    for (int k0 = 8; k0 < ns; k0 += 8) {
+    for (int k0 = Q; k0 < ns; k0 += 8) {
       f32x4_t c0[8], c1[8];
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
@@ -214,7 +215,8 @@ __global__ __launch_bounds__(64 * kWaveRows) void combine_wave_kernel(CombinePar
   if (row >= p.rows) return;                      // the whole wave leaves; no barrier below
   const int rows[1] = {row};
   float u[1][8], lse[1];
-  combine_rows<1>(p, rows, lane, u, lse);
+  if (p.n_split <= 4) combine_rows<1, 4>(p, rows, lane, u, lse);
+  else combine_rows<1>(p, rows, lane, u, lse);
   store_u_row(p, row, lane, u[0], lse[0]);
 }
 
@@ -257,7 +259,8 @@ __global__ __launch_bounds__(kOutThreads) void combine_out_kernel(CombineParams 
   if (n0 + 1 < p.n_tok) {                          // wave-uniform
     const int rows[2] = {n0 * p.H + h, (n0 + 1) * p.H + h};
     float u[2][8], lse[2];
-    combine_rows<2>(p, rows, lane, u, lse);
+    if (p.n_split <= 4) combine_rows<2, 4>(p, rows, lane, u, lse);
+    else combine_rows<2>(p, rows, lane, u, lse);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
@@ -267,7 +270,8 @@ __global__ __launch_bounds__(kOutThreads) void combine_out_kernel(CombineParams 
   } else if (n0 < p.n_tok) {
     const int rows[1] = {n0 * p.H + h};
     float u[1][8], lse[1];
-    combine_rows<1>(p, rows, lane, u, lse);
+    if (p.n_split <= 4) combine_rows<1, 4>(p, rows, lane, u, lse);
+    else combine_rows<1>(p, rows, lane, u, lse);
 #pragma unroll
     for (int i = 0; i < 4; ++i) packed[0][i] = pack_bf16x2(u[0][2 * i], u[0][2 * i + 1]);
     if (p.out) store_u_row(p, rows[0], lane, u[0], lse[0]);
