@@ -211,7 +211,10 @@ typedef struct mla_decode_args {
  * mla_decode_plan -- host-only: the split size, split count and workspace
  * bytes mla_decode_paged will use for these arguments (pointers may be NULL).
  * With more than one split, each (sequence, split, 64-row group) produces
- * fp32 partials (m, l, U) merged by a log-sum-exp combine kernel.
+ * partials merged by a log-sum-exp combine kernel: fp32 (m, l) per row and
+ * the split's latent aggregate, as fp32 U when out_dt is F32 and as bf16
+ * u = U / l when out_dt is BF16 (bf16 and fp8 pools), so the workspace size
+ * depends on out_dt.
  */
 int mla_decode_plan(const mla_decode_args* args, int* split_tokens, int* n_split,
                     size_t* workspace_bytes);

@@ -4,6 +4,8 @@
 // sum of 2^(z - m_k) and the unnormalised latent aggregate. With
 // m* = max_k m_k and w_k = 2^(m_k - m*):
 //   u = (sum_k w_k U_k) / (sum_k w_k l_k),  lse = (m* + log2 sum_k w_k l_k) ln 2.
+// When the output is bf16 the splits store u_k = U_k / l_k in bf16 instead
+// (half the bytes), and u = sum_k a_k u_k with a_k = w_k l_k / sum_j w_j l_j.
 // Only splits k < ceil(L_b / split_tokens) exist (units past the end of a
 // sequence write nothing); a row that sees no token of an existing split
 // carries (-inf, 0, 0) there and gets weight 0. The latent sums run over k
@@ -60,11 +62,18 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
   for (int k = 1; k < ns; ++k) lsum = fmaf(wsh[k], ml(k)[1], lsum);
 
   const int d = 4 * tid;
-  const f32x4_t* pu = (const f32x4_t*)(p.part_u + (((size_t)b * nsp) * p.R + r) * kDc + d);
-  const size_t kstride = (size_t)p.R * kDc / 4;
-  f32x4_t acc = wsh[0] * pu[0];
+  const size_t e0 = (((size_t)b * nsp) * p.R + r) * kDc + d;   // element of split 0
+  const size_t kstride = (size_t)p.R * kDc;
+  // split k's 4 values (bf16 partials: l_k u_k, so that acc / lsum is u)
+  auto part = [&](int k) -> f32x4_t {
+    if (!p.part_bf16) return *(const f32x4_t*)((const float*)p.part_u + e0 + k * kstride);
+    const u32x2_t h = *(const u32x2_t*)((const uint16_t*)p.part_u + e0 + k * kstride);
+    const float lk = ml(k)[1];
+    return (f32x4_t){bf2f(h[0] & 0xffff), bf2f(h[0] >> 16), bf2f(h[1] & 0xffff), bf2f(h[1] >> 16)} * lk;
+  };
+  f32x4_t acc = wsh[0] * part(0);
   for (int k = 1; k < ns; ++k) {
-    const f32x4_t v = pu[k * kstride];
+    const f32x4_t v = part(k);
     const float wk = wsh[k];
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] = fmaf(wk, v[i], acc[i]);
@@ -108,8 +117,14 @@ __device__ __forceinline__ float wave_sum64(float v) {
 // allocated n_split; Q = 4 when no more are allocated) is issued before the
 // sequence length is known, so one memory round trip serves all NR rows;
 // splits past the live count are then masked out and never accumulated. The
-// sum runs over k in increasing order whatever Q is.
-template <int NR, int Q = 8>
+// sum runs over k in increasing order whatever Q is. PB: the partials are
+// bf16 u_k (16 bytes per lane and split) weighted by a_k = w_k l_k / sum.
+__device__ __forceinline__ void unpack_bf16x8(const u32x4_t& h, f32x4_t& lo, f32x4_t& hi) {
+  lo = (f32x4_t){bf2f(h[0] & 0xffff), bf2f(h[0] >> 16), bf2f(h[1] & 0xffff), bf2f(h[1] >> 16)};
+  hi = (f32x4_t){bf2f(h[2] & 0xffff), bf2f(h[2] >> 16), bf2f(h[3] & 0xffff), bf2f(h[3] >> 16)};
+}
+
+template <int NR, int Q, bool PB>
 __device__ __forceinline__ void combine_rows(const CombineParams& p, const int (&row)[NR], int lane,
                                              float (&u)[NR][8], float (&lse_out)[NR]) {
   const int nsp = p.n_split;                                   // split stride in memory
@@ -117,7 +132,9 @@ __device__ __forceinline__ void combine_rows(const CombineParams& p, const int (
   int Ls[NR];
   float mk[NR], lk[NR];
   f32x4_t v0[NR][Q], v1[NR][Q];
+  u32x4_t vb[NR][Q];
   const float* pu[NR];
+  const uint16_t* pb[NR];
 #pragma unroll
   for (int t = 0; t < NR; ++t) {
     const int b = row[t] / p.R, r = row[t] % p.R;
@@ -125,12 +142,18 @@ __device__ __forceinline__ void combine_rows(const CombineParams& p, const int (
     const float* ml = p.part_ml + (((size_t)b * nsp + min(lane, nsp - 1)) * p.R + r) * 2;
     mk[t] = ml[0];
     lk[t] = ml[1];
-    pu[t] = p.part_u + (((size_t)b * nsp) * p.R + r) * kDc + 8 * lane;
+    const size_t e0 = (((size_t)b * nsp) * p.R + r) * kDc + 8 * lane;
+    pu[t] = (const float*)p.part_u + e0;
+    pb[t] = (const uint16_t*)p.part_u + e0;
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
       const size_t off = (size_t)min(q, nsp - 1) * kstride;
-      v0[t][q] = *(const f32x4_t*)(pu[t] + off);
-      v1[t][q] = *(const f32x4_t*)(pu[t] + off + 4);
+      if constexpr (PB) {
+        vb[t][q] = *(const u32x4_t*)(pb[t] + off);
+      } else {
+        v0[t][q] = *(const f32x4_t*)(pu[t] + off);
+        v1[t][q] = *(const f32x4_t*)(pu[t] + off + 4);
+      }
     }
   }
 #pragma unroll
@@ -150,14 +173,20 @@ __device__ __forceinline__ void combine_rows(const CombineParams& p, const int (
     const float wk = (m_l == -INFINITY) ? 0.f : exp2f(m_l - mx);
     const float lsum = wave_sum64(wk * l_l);
     // split 0 is always live (L >= T >= 1); the split weights come from the
-    // lane that holds them (k is wave-uniform)
-    const float w0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk), 0));
+    // lane that holds them (k is wave-uniform); bf16 partials take
+    // a_k = w_k l_k / lsum (1 for a single live split)
+    const float wa = PB ? wk * l_l / lsum : wk;
+    if constexpr (PB) {
+#pragma unroll
+      for (int q = 0; q < Q; ++q) unpack_bf16x8(vb[t][q], v0[t][q], v1[t][q]);
+    }
+    const float w0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wa), 0));
     f32x4_t acc0 = w0 * v0[t][0];
     f32x4_t acc1 = w0 * v1[t][0];
 #pragma unroll
     for (int q = 1; q < Q; ++q) {
       if (q < ns) {
-        const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk), q));
+        const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wa), q));
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           acc0[i] = fmaf(w, v0[t][q][i], acc0[i]);
@@ -167,16 +196,25 @@ __device__ __forceinline__ void combine_rows(const CombineParams& p, const int (
     }
     for (int k0 = Q; k0 < ns; k0 += 8) {
       f32x4_t c0[8], c1[8];
+      u32x4_t cb[8];
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         const size_t off = (size_t)min(k0 + q, ns - 1) * kstride;
-        c0[q] = *(const f32x4_t*)(pu[t] + off);
-        c1[q] = *(const f32x4_t*)(pu[t] + off + 4);
+        if constexpr (PB) {
+          cb[q] = *(const u32x4_t*)(pb[t] + off);
+        } else {
+          c0[q] = *(const f32x4_t*)(pu[t] + off);
+          c1[q] = *(const f32x4_t*)(pu[t] + off + 4);
+        }
+      }
+      if constexpr (PB) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) unpack_bf16x8(cb[q], c0[q], c1[q]);
       }
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         if (k0 + q < ns) {
-          const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk), k0 + q));
+          const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wa), k0 + q));
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             acc0[i] = fmaf(w, c0[q][i], acc0[i]);
@@ -187,10 +225,24 @@ __device__ __forceinline__ void combine_rows(const CombineParams& p, const int (
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      u[t][i] = acc0[i] / lsum;
-      u[t][4 + i] = acc1[i] / lsum;
+      u[t][i] = PB ? acc0[i] : acc0[i] / lsum;
+      u[t][4 + i] = PB ? acc1[i] : acc1[i] / lsum;
     }
     lse_out[t] = (mx + log2f(lsum)) * kLn2;
+  }
+}
+
+// combine_rows with the partial format and the number of up-front loads
+// (4 when no more splits are allocated) chosen at run time
+template <int NR>
+__device__ __forceinline__ void combine_rows_any(const CombineParams& p, const int (&row)[NR], int lane,
+                                                 float (&u)[NR][8], float (&lse_out)[NR]) {
+  if (p.part_bf16) {
+    if (p.n_split <= 4) combine_rows<NR, 4, true>(p, row, lane, u, lse_out);
+    else combine_rows<NR, 8, true>(p, row, lane, u, lse_out);
+  } else {
+    if (p.n_split <= 4) combine_rows<NR, 4, false>(p, row, lane, u, lse_out);
+    else combine_rows<NR, 8, false>(p, row, lane, u, lse_out);
   }
 }
 
@@ -215,8 +267,7 @@ __global__ __launch_bounds__(64 * kWaveRows) void combine_wave_kernel(CombinePar
   if (row >= p.rows) return;                      // the whole wave leaves; no barrier below
   const int rows[1] = {row};
   float u[1][8], lse[1];
-  if (p.n_split <= 4) combine_rows<1, 4>(p, rows, lane, u, lse);
-  else combine_rows<1>(p, rows, lane, u, lse);
+  combine_rows_any<1>(p, rows, lane, u, lse);
   store_u_row(p, row, lane, u[0], lse[0]);
 }
 
@@ -259,8 +310,7 @@ __global__ __launch_bounds__(kOutThreads) void combine_out_kernel(CombineParams 
   if (n0 + 1 < p.n_tok) {                          // wave-uniform
     const int rows[2] = {n0 * p.H + h, (n0 + 1) * p.H + h};
     float u[2][8], lse[2];
-    if (p.n_split <= 4) combine_rows<2, 4>(p, rows, lane, u, lse);
-    else combine_rows<2>(p, rows, lane, u, lse);
+    combine_rows_any<2>(p, rows, lane, u, lse);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
@@ -270,8 +320,7 @@ __global__ __launch_bounds__(kOutThreads) void combine_out_kernel(CombineParams 
   } else if (n0 < p.n_tok) {
     const int rows[1] = {n0 * p.H + h};
     float u[1][8], lse[1];
-    if (p.n_split <= 4) combine_rows<1, 4>(p, rows, lane, u, lse);
-    else combine_rows<1>(p, rows, lane, u, lse);
+    combine_rows_any<1>(p, rows, lane, u, lse);
 #pragma unroll
     for (int i = 0; i < 4; ++i) packed[0][i] = pack_bf16x2(u[0][2 * i], u[0][2 * i + 1]);
     if (p.out) store_u_row(p, rows[0], lane, u[0], lse[0]);

@@ -42,8 +42,9 @@
 // and is folded into the probability for the aggregation, P' = p * scale_s,
 // which reads the codes transposed (ds_read_b64_tr_b8).
 //
-// The split ends by writing either u = U / l and lse, or fp32 partials
-// (m, l, U) for the log-sum-exp combine kernel.
+// The split ends by writing either u = U / l and lse, or partials (m, l and
+// U in fp32, or u = U / l in bf16 when the output is bf16) for the
+// log-sum-exp combine kernel; bf16 rows leave through LDS in 1-KB stores.
 #include "dma.h"
 #include "mla_device.h"
 #include "mla_internal.h"
@@ -121,6 +122,13 @@ __device__ __forceinline__ int swz_p(int r) {
 // Rope rows (128 B): chunk j (0..7) of token t lives at chunk j ^ ((t>>1)&7).
 __device__ __forceinline__ int swz_rope(int t) { return (t >> 1) & 7; }
 
+// The split's u = U / l leaves as bf16 through an LDS staging area (the
+// direct bf16 output, and bf16 partials), else as fp32 from registers.
+__device__ __forceinline__ bool stage_u(const DecodeParams& p) {
+  return p.n_split == 1 ? p.out_bf16 != 0 : p.part_bf16 != 0;
+}
+constexpr int kStagePitch = 1024 + 16;   // bf16 row of 512 + 16 B (rows 4 banks apart)
+
 // 8 E4M3FN bytes -> 8 bf16 (exact: every E4M3FN value is a bf16 value).
 __device__ __forceinline__ bf16x8_t fp8x8_to_bf16(const i32x2_t& v) {
   typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
@@ -144,7 +152,9 @@ __device__ void write_uniform_result(const DecodeParams& p, int b, int k, int g,
       if (p.out_bf16) ((uint16_t*)p.out)[o] = f2bf(v);
       else ((float*)p.out)[o] = v;
     } else {
-      p.part_u[(((size_t)b * p.n_split + k) * p.R + r) * kDc + d] = v;
+      const size_t o = (((size_t)b * p.n_split + k) * p.R + r) * kDc + d;
+      if (p.part_bf16) ((uint16_t*)p.part_u)[o] = f2bf(v);
+      else ((float*)p.part_u)[o] = v;
     }
   }
   for (int r = r0 + tid; r < r0 + nrows; r += kThreads) {
@@ -420,6 +430,7 @@ void decode_mfma_kernel(DecodeParams p) {
       }
     }
     lds_barrier();  // (Z) row sums and reference maxima published
+    if (stage_u(p)) lds_barrier();   // (W) the aggregation team's u staged
     return;
   }
 
@@ -611,7 +622,39 @@ void decode_mfma_kernel(DecodeParams p) {
   }
   lds_barrier();  // (Z) row sums and reference maxima published
 
-  // ---- finish: u = U / l or fp32 partials ----------------------------------
+  // ---- finish: u = U / l, or partials (m, l, U or u) ------------------------
+  const bool direct = p.n_split == 1;
+  const size_t row_base = direct ? (size_t)b * p.R : ((size_t)b * p.n_split + k) * p.R;
+  if (stage_u(p)) {
+    // bf16 u = U / l (0 for a row that saw no token of the split) into LDS
+    // (the tile buffers are free after (Z)), then one 1-KB store per row
+    lds_char* const stg = smem;   // [64 rows][kStagePitch]
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rr = 16 * rt + 4 * G4 + i;
+        const float lval = lsum[rr] + lsum[64 + rr];
+        // one reciprocal per row: U * (1/l) is within 1 ulp of U / l, and
+        // a bf16 value v stays v (U = v * l rounds back to v)
+        const float inv = lval > 0.f ? 1.f / lval : 0.f;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          const float u = U[rt][dt][i] * inv;
+          *(MLA_LDS uint16_t*)(stg + rr * kStagePitch + (128 * v + 16 * dt + i16) * 2) = f2bf(u);
+        }
+      }
+    lds_barrier();  // (W) u staged
+    uint16_t* const dst = direct ? (uint16_t*)p.out : (uint16_t*)p.part_u;
+#pragma unroll 4
+    for (int s = 0; s < 16; ++s) {
+      const int rr = 16 * v + s;
+      if (row0 + rr >= p.R) break;   // wave-uniform
+      const u32x4_t val = *(const MLA_LDS u32x4_t*)(stg + rr * kStagePitch + lane * 16);
+      *(u32x4_t*)(dst + (row_base + row0 + rr) * kDc + 8 * lane) = val;
+    }
+  }
+  // row statistics (and fp32 u or U straight from registers)
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
@@ -621,23 +664,18 @@ void decode_mfma_kernel(DecodeParams p) {
       if (r >= p.R) continue;
       const float lval = lsum[rr] + lsum[64 + rr];
       const float mval = mbuf[rr];
-      if (p.n_split == 1) {
-        const size_t o = ((size_t)b * p.R + r) * kDc + 128 * v + i16;
+      if (!stage_u(p)) {
+        const size_t o = (row_base + r) * kDc + 128 * v + i16;
+        float* const dst = direct ? (float*)p.out : (float*)p.part_u;
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-          const float u = U[rt][dt][i] / lval;
-          if (p.out_bf16) ((uint16_t*)p.out)[o + 16 * dt] = f2bf(u);
-          else ((float*)p.out)[o + 16 * dt] = u;
-        }
-        if (p.lse && v == 0 && i16 == 0) p.lse[(size_t)b * p.R + r] = (mval + log2f(lval)) * kLn2;
-      } else {
-        const size_t base = ((size_t)b * p.n_split + k) * p.R + r;
-        float* pu = p.part_u + base * kDc + 128 * v + i16;
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) pu[16 * dt] = U[rt][dt][i];
-        if (v == 0 && i16 == 0) {
-          p.part_ml[base * 2] = mval;
-          p.part_ml[base * 2 + 1] = lval;
+        for (int dt = 0; dt < 8; ++dt) dst[o + 16 * dt] = direct ? U[rt][dt][i] / lval : U[rt][dt][i];
+      }
+      if (v == 0 && i16 == 0) {
+        if (direct) {
+          if (p.lse) p.lse[(size_t)b * p.R + r] = (mval + log2f(lval)) * kLn2;
+        } else {
+          p.part_ml[(row_base + r) * 2] = mval;
+          p.part_ml[(row_base + r) * 2 + 1] = lval;
         }
       }
     }

@@ -138,8 +138,9 @@ __global__ __launch_bounds__(kThreads) void decode_simple_f32_kernel(DecodeParam
     if (p.lse && tid == 0) p.lse[(size_t)b * p.R + r] = (M + log2f(lsum)) * kLn2;
   } else {
     const size_t base = ((size_t)b * p.n_split + k) * p.R + r;
-    p.part_u[base * kDc + tid] = U[0];
-    p.part_u[base * kDc + tid + kThreads] = U[1];
+    float* const pu = (float*)p.part_u + base * kDc;   // fp32 caches keep fp32 partials
+    pu[tid] = U[0];
+    pu[tid + kThreads] = U[1];
     if (tid == 0) {
       p.part_ml[base * 2] = M;
       p.part_ml[base * 2 + 1] = lsum;

@@ -53,6 +53,10 @@ int check_shape(const mla_decode_args* a) {
   return MLA_OK;
 }
 
+// Split partials are bf16 (the normalised u of each split) exactly when the
+// output is bf16 and the MFMA kernel runs; fp32 outputs keep fp32 partials.
+bool part_bf16(const mla_decode_args* a) { return a->out_dt == MLA_BF16 && a->ckv_dt != MLA_F32; }
+
 Plan make_plan(const mla_decode_args* a) {
   Plan pl;
   const int64_t R = (int64_t)a->T * a->H;
@@ -82,7 +86,9 @@ Plan make_plan(const mla_decode_args* a) {
   pl.n_split = (int)((Lmax + pl.split_tokens - 1) / pl.split_tokens);
   if (pl.n_split > 1) {
     const size_t parts = (size_t)a->B * pl.n_split * R;
-    pl.part_u_bytes = align_up(parts * kDc * sizeof(float), kWsAlign);
+    // bf16 output from a bf16 / fp8 cache: partials hold bf16 u = U / l
+    const size_t elt = part_bf16(a) ? 2 : sizeof(float);
+    pl.part_u_bytes = align_up(parts * kDc * elt, kWsAlign);
     pl.ws_bytes = pl.part_u_bytes + align_up(parts * 2 * sizeof(float), kWsAlign);
   }
   return pl;
@@ -239,7 +245,8 @@ int mla_decode_paged(const mla_decode_args* a, void* stream) {
   p.seq_lens = a->seq_lens;
   p.out = a->out;
   p.lse = a->lse;
-  p.part_u = pl.n_split > 1 ? (float*)a->workspace : nullptr;
+  p.part_u = pl.n_split > 1 ? a->workspace : nullptr;
+  p.part_bf16 = part_bf16(a);
   p.part_ml = pl.n_split > 1 ? (float*)((char*)a->workspace + pl.part_u_bytes) : nullptr;
   p.B = a->B;
   p.T = a->T;
@@ -268,6 +275,7 @@ int mla_decode_paged(const mla_decode_args* a, void* stream) {
     CombineParams c{};
     c.part_u = p.part_u;
     c.part_ml = p.part_ml;
+    c.part_bf16 = p.part_bf16;
     c.out = a->out;
     c.lse = a->lse;
     c.seq_lens = a->seq_lens;

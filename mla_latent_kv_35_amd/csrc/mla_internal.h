@@ -31,8 +31,9 @@ struct DecodeParams {
   const int32_t* seq_lens;
   void* out;                // [B][R][512]
   float* lse;               // [B][R] or null
-  float* part_u;            // [B][n_split][R][512] fp32 (n_split > 1)
+  void* part_u;             // [B][n_split][R][512] (n_split > 1): fp32 U, or bf16 u = U / l
   float* part_ml;           // [B][n_split][R][2]   fp32 (m in log2 units, l)
+  int part_bf16;            // partials hold bf16 u = U / l (0 where l = 0)
   int B, T, H, R;           // R = T*H query rows per sequence
   int G;                    // row groups per sequence (MFMA kernel)
   int n_split, split_tokens;
@@ -44,8 +45,9 @@ struct DecodeParams {
 };
 
 struct CombineParams {
-  const float* part_u;
+  const void* part_u;       // as DecodeParams::part_u
   const float* part_ml;
+  int part_bf16;
   void* out;
   float* lse;
   const int32_t* seq_lens;  // splits at or past L_b hold no partials

@@ -67,7 +67,12 @@ def test_plan_for_the_five_workloads(B):
                                      max_seq_len=31804, total_tokens=1055283))
     assert st % 64 == 0 and ns == -(-31804 // st)
     parts = 64 * ns * 128
-    assert ws == ((parts * 512 * 4 + 255) // 256) * 256 + ((parts * 8 + 255) // 256) * 256
+    # bf16 output: bf16 u per partial row, then fp32 (m, l)
+    assert ws == ((parts * 512 * 2 + 255) // 256) * 256 + ((parts * 8 + 255) // 256) * 256
+    # fp32 output from the same pool: fp32 U
+    _, _, ws32 = B.decode_plan(_args(B, B=64, n_pages=16522, max_pages_per_seq=497,
+                                     max_seq_len=31804, total_tokens=1055283, out_dt=B.MLA_F32))
+    assert ws32 == ((parts * 512 * 4 + 255) // 256) * 256 + ((parts * 8 + 255) // 256) * 256
     # fp32 tiny
     st, ns, _ = B.decode_plan(_args(B, B=1, H=16, q_dt=0, ckv_dt=0, kr_dt=0, out_dt=0,
                                     n_pages=4, max_pages_per_seq=4, max_seq_len=256))

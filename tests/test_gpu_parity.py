@@ -131,6 +131,15 @@ def test_small_fp8_parity(mla, kw, split):
     check_against_oracle(mla, synth.make_inputs(cfg), split_tokens=split)
 
 
+@pytest.mark.parametrize("dts", [dict(), dict(ckv_dt="fp8"),
+                                 dict(q_dt="f32", ckv_dt="f32", kr_dt="f32")])
+def test_more_splits_than_wave_lanes(mla, dts):
+    """70 one-page splits: the one-workgroup-per-row combine (more splits than
+    a wave has lanes), over bf16 partials (bf16 and fp8 pools) and fp32 ones."""
+    cfg = synth.small_config(B=2, H=16, T=1, seq_len=64 * 70, ragged=False, seed=61, **dts)
+    check_against_oracle(mla, synth.make_inputs(cfg), split_tokens=64)
+
+
 # --------------------------------------------------------------------------
 # the five workloads at full size
 # --------------------------------------------------------------------------
