@@ -60,7 +60,7 @@ def copy_probe(mib: int) -> None:
 
 def kernel_source_digest() -> str:
     h = hashlib.sha256()
-    for f in ("decode_mfma.hip", "combine.hip", "mla_device.h", "mla_internal.h"):
+    for f in ("decode_mfma.hip", "combine.hip", "dma.h", "mla_device.h", "mla_internal.h"):
         with open(os.path.join(ROOT, "mla_latent_kv_35_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
