@@ -140,6 +140,32 @@ def test_more_splits_than_wave_lanes(mla, dts):
     check_against_oracle(mla, synth.make_inputs(cfg), split_tokens=64)
 
 
+@pytest.mark.parametrize("ckv_dt", ["bf16", "fp8"])
+@pytest.mark.parametrize("split", [0, 64])
+def test_f32_output_from_bf16_and_fp8_pools(mla, ckv_dt, split):
+    """u in fp32 from the MFMA kernel: with splits the partials are fp32 U
+    merged by the combine, with one split u is written directly; both against
+    the oracle, and the bf16 output of the same call within one bf16 step."""
+    cfg = synth.small_config(B=3, H=128, T=1, seq_len=700, ragged=True, permuted=True, seed=77,
+                             ckv_dt=ckv_dt)
+    inp = synth.make_inputs(cfg)
+    d = mla.upload(inp)
+    q_lat = mla.absorb_q(d.q_nope, d.w_uk)
+    q_rot = mla.rope(d.q_rope, d.positions)
+    u32, lse32 = mla.decode_paged(q_lat, q_rot, d.cache, 1, cfg.softmax_scale,
+                                  out_dtype=torch.float32, split_tokens=split)
+    u16, lse16 = mla.decode_paged(q_lat, q_rot, d.cache, 1, cfg.softmax_scale,
+                                  out_dtype=torch.bfloat16, split_tokens=split)
+    torch.cuda.synchronize()
+    ref = O.decode_step(inp)
+    g = host(u32)
+    assert row_rel(g, np.stack([ref[b]["u"][0] for b in ref])) <= TOL[ckv_dt]
+    assert np.abs(host(lse32) - np.stack([ref[b]["lse"][0] for b in ref])).max() <= 5e-2
+    # the bf16 output is the fp32 one rounded, up to the partials' own bf16 step
+    assert row_rel(host(u16), g) <= 2 ** -7
+    assert np.array_equal(host(lse16), host(lse32))
+
+
 # --------------------------------------------------------------------------
 # the five workloads at full size
 # --------------------------------------------------------------------------
