@@ -178,7 +178,8 @@ typedef struct mla_decode_args {
   int32_t ckv_dt;           /* latent pool: F32, BF16 or FP8_E4M3 */
   int32_t kr_dt;            /* rope pool: F32 (iff ckv_dt is F32) or BF16 */
   int32_t out_dt;           /* u: F32 or BF16 */
-  int32_t split_tokens;     /* 0 = auto; else a multiple of 64: split k covers
+  int32_t split_tokens;     /* 0 = auto; else a multiple of 64, at most 65536
+                               (MLA_ERR_UNSUPPORTED above): split k covers
                                tokens [k*split_tokens, (k+1)*split_tokens) */
   int64_t total_tokens;     /* host hint: sum of seq_lens (0 = unknown) */
   float softmax_scale;      /* 1/sqrt(d_h + d_r) for DeepSeek-V2 (eq. 18) */

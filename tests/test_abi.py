@@ -81,10 +81,12 @@ def test_plan_for_the_five_workloads(B):
 
 @pytest.mark.parametrize("field,value,status", [
     ("T", 3, 4), ("d_c", 256, 4), ("page_size", 32, 4), ("max_seq_len", 0, 2),
-    ("max_seq_len", 64 * 64 + 1, 2), ("split_tokens", 100, 2), ("reserved0", 1, 2),
+    ("max_seq_len", 64 * 64 + 1, 2), ("split_tokens", 100, 2), ("split_tokens", 65536 + 64, 4),
+    ("reserved0", 1, 2),
     ("softmax_scale", 0.0, 2), ("kr_dt", 0, 3), ("ckv_dt", 7, 3), ("B", 0, 2),
 ])
 def test_plan_rejects_bad_shapes(B, field, value, status):
+    # a split of at most 1024 pages (65536 tokens): the split kernel keeps its page ids in LDS
     st = B.lib().mla_decode_plan(ctypes.byref(_args(B, **{field: value})), None, None, None)
     assert st == status
 
