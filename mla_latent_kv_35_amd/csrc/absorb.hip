@@ -2,11 +2,13 @@
 // analysis", section 1.2 and section 6): q_lat[n][h][:] = W_UK[h]^T q[n][h][:],
 // so the score q^T (W^UK c) becomes q_lat . c against the cached latent.
 //
-// bf16: one workgroup per (head h, 128-wide latent block, 32 tokens), the
-// blocks of one head on one XCD. The weight block W_UK[h][0:128][d0:d0+128] is staged in LDS with the same
-// 16-byte XOR swizzle the decode kernel uses and read transposed
-// (ds_read_b64_tr_b16) as the K-major MFMA operand; the queries are read
-// straight from global memory as the other operand. fp32: plain fp32 FMA.
+// bf16: one workgroup per (head h, 128-wide latent block), the blocks of one
+// head on one XCD. The weight block W_UK[h][0:128][d0:d0+128] is staged in
+// LDS once, with the same 16-byte XOR swizzle the decode kernel uses, and read
+// transposed (ds_read_b64_tr_b16) as the K-major MFMA operand; the workgroup
+// then walks the tokens in blocks of 32, staging each block's queries in LDS
+// (double-buffered, the next block's loads in flight during the current
+// block's MFMAs) as the other operand. fp32: plain fp32 FMA.
 #include "mla_device.h"
 #include "mla_extra.h"
 #include "mla_internal.h"
@@ -20,37 +22,49 @@ constexpr int kTokTile = 32;
 
 __device__ __forceinline__ int swz16(int s) { return (s & 8) | ((s & 3) << 1) | ((s >> 2) & 1); }
 
-constexpr int kAbsorbLds = kDh * 256;   // the staged 128 x 128 bf16 weight block
+constexpr int kWBlock = kDh * 256;                 // the staged 128 x 128 bf16 weight block
+constexpr int kQBlock = kTokTile * kDh * 2;        // one block of 32 tokens' queries: 8 KB
+constexpr int kAbsorbLds = kWBlock + 2 * kQBlock;  // 48 KB: three workgroups per CU
+
+// Query rows staged in LDS: 256 B per token, 16-byte chunk c at c ^ (t & 15),
+// so the 16 tokens of an MFMA A fragment read 16 distinct bank groups.
+__device__ __forceinline__ int q_chunk(int t, int c) { return c ^ (t & 15); }
 
 template <bool OUT_BF16>
 __device__ __forceinline__ void absorb_bf16_block(int bid, lds_char* smem,
                                                   const uint16_t* __restrict__ q,
                                                   const uint16_t* __restrict__ wuk,
-                                                  void* __restrict__ out, int n_tok, int H,
-                                                  int n_tb) {
+                                                  void* __restrict__ out, int n_tok, int H) {
   // blocks on XCD x (= bid % 8) serve the heads h with h % 8 == x
   const int x = bid % kNumXcd, idx = bid / kNumXcd;
-  const int per_head = 4 * n_tb;
-  const int h = kNumXcd * (idx / per_head) + x;
+  const int h = kNumXcd * (idx >> 2) + x;
   if (h >= H) return;
-  const int tb = (idx % per_head) >> 2;
   const int d0 = 128 * (idx & 3);
-  const int n0 = tb * kTokTile;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int i16 = lane & 15, G4 = lane >> 4;
+  const int n_tb = (n_tok + kTokTile - 1) / kTokTile;
 
-  // queries of the block's 32 tokens (A operand rows) and the weight block
-  // W_UK[h][0:128][d0:d0+128] are both in flight before anything waits
-  bf16x8_t a[2][4];
+  // query chunks of token block tb this thread moves: 32 tokens x 16 chunks
+  // of 16 B = 512 chunks, 2 per thread (token t = e / 16, chunk c = e % 16)
+  u32x4_t qv[kQBlock / 16 / kThreads];
+  auto load_q = [&](int tb) __attribute__((always_inline)) {
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    const int na = n0 + 16 * tt + i16;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      if (na < n_tok) a[tt][ks] = load_bf16x8(q + ((size_t)na * H + h) * kDh + 32 * ks + 8 * G4);
-      else a[tt][ks] = (bf16x8_t){0, 0, 0, 0, 0, 0, 0, 0};
+    for (int i = 0; i < kQBlock / 16 / kThreads; ++i) {
+      const int e = tid + kThreads * i, t = e >> 4, c = e & 15;
+      const int n = tb * kTokTile + t;
+      qv[i] = (u32x4_t){0u, 0u, 0u, 0u};
+      if (n < n_tok) qv[i] = *(const u32x4_t*)(q + ((size_t)n * H + h) * kDh + 8 * c);
     }
-  }
+  };
+  auto store_q = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kQBlock / 16 / kThreads; ++i) {
+      const int e = tid + kThreads * i, t = e >> 4, c = e & 15;
+      *(MLA_LDS u32x4_t*)(smem + kWBlock + buf * kQBlock + t * 256 + q_chunk(t, c) * 16) = qv[i];
+    }
+  };
+  // the weight block W_UK[h][0:128][d0:d0+128] and the first queries are in
+  // flight before anything waits
   const uint16_t* wh = wuk + (size_t)h * kDh * kDc + d0;
   u32x4_t wv[(kDh * 16) / kThreads];
 #pragma unroll
@@ -59,6 +73,7 @@ __device__ __forceinline__ void absorb_bf16_block(int bid, lds_char* smem,
     const int j = idx2 >> 4, c = idx2 & 15;
     wv[e] = *(const u32x4_t*)(wh + (size_t)j * kDc + 8 * c);
   }
+  load_q(0);
   // stage the weight block: row j = 16 chunks of 16 B, chunk c at c ^ swz16(j & 15)
 #pragma unroll
   for (int e = 0; e < (kDh * 16) / kThreads; ++e) {
@@ -66,9 +81,11 @@ __device__ __forceinline__ void absorb_bf16_block(int bid, lds_char* smem,
     const int j = idx2 >> 4, c = idx2 & 15;
     *(MLA_LDS u32x4_t*)(smem + j * 256 + ((c ^ swz16(j & 15)) * 16)) = wv[e];
   }
+  store_q(0);
   __syncthreads();
 
-  // B operands (K = j, N = d) for this wave's two 16-wide d tiles
+  // B operands (K = j, N = d) for this wave's two 16-wide d tiles, kept for
+  // every token block
   const int xq = 4 * (G4 & 1) + (i16 >> 2);
   const int c0 = (i16 & 3) >> 1;
   bf16x8_t bw[2][4];
@@ -83,33 +100,49 @@ __device__ __forceinline__ void absorb_bf16_block(int bid, lds_char* smem,
       bw[u][ks] = concat(lo, hi);
     }
   }
+  for (int tb = 0; tb < n_tb; ++tb) {
+    if (tb + 1 < n_tb) load_q(tb + 1);
+    const lds_char* const qs = smem + kWBlock + (tb & 1) * kQBlock;
+    const int n0 = tb * kTokTile;
+    const int n_tt = min(2, (n_tok - n0 + 15) >> 4);   // 16-token blocks with a live token
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt)
+    for (int tt = 0; tt < 2; ++tt) {
+      if (tt >= n_tt) break;                              // uniform
+      const int t = 16 * tt + i16;
+      bf16x8_t a[4];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      for (int ks = 0; ks < 4; ++ks) a[ks] = lds_read_b128(qs + t * 256 + q_chunk(t, 4 * ks + G4) * 16);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) acc = mfma16x16x32(a[tt][ks], bw[u][ks], acc);
-      const int d = d0 + 16 * (2 * w + u) + i16;
+      for (int u = 0; u < 2; ++u) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int n = n0 + 16 * tt + 4 * G4 + i;
-        if (n < n_tok) {
-          const size_t o = ((size_t)n * H + h) * kDc + d;
-          if (OUT_BF16) ((uint16_t*)out)[o] = f2bf(acc[i]);
-          else ((float*)out)[o] = acc[i];
+        for (int ks = 0; ks < 4; ++ks) acc = mfma16x16x32(a[ks], bw[u][ks], acc);
+        const int d = d0 + 16 * (2 * w + u) + i16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int n = n0 + 16 * tt + 4 * G4 + i;
+          if (n < n_tok) {
+            const size_t o = ((size_t)n * H + h) * kDc + d;
+            if (OUT_BF16) ((uint16_t*)out)[o] = f2bf(acc[i]);
+            else ((float*)out)[o] = acc[i];
+          }
         }
       }
     }
+    if (tb + 1 < n_tb) {
+      store_q((tb + 1) & 1);   // that buffer was last read in block tb-1, before the barrier
+      __syncthreads();
+    }
+  }
 }
 
 template <bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) void absorb_bf16_kernel(const uint16_t* __restrict__ q,
                                                                const uint16_t* __restrict__ wuk,
                                                                void* __restrict__ out, int n_tok,
-                                                               int H, int n_tb) {
+                                                               int H) {
   __shared__ __attribute__((aligned(16))) char smem[kAbsorbLds];
-  absorb_bf16_block<OUT_BF16>(blockIdx.x, (lds_char*)smem, q, wuk, out, n_tok, H, n_tb);
+  absorb_bf16_block<OUT_BF16>(blockIdx.x, (lds_char*)smem, q, wuk, out, n_tok, H);
 }
 
 // The query side of one decode step in one launch: the first n_abs blocks
@@ -120,12 +153,12 @@ __global__ __launch_bounds__(kThreads) void absorb_bf16_kernel(const uint16_t* _
 template <bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) void absorb_rope_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ wuk, void* __restrict__ out,
-    int n_tok, int H, int n_tb, int n_abs, const uint16_t* q_rope, uint16_t* q_rot,
+    int n_tok, int H, int n_abs, const uint16_t* q_rope, uint16_t* q_rot,
     const int32_t* pos, double base, const double* freq) {
   __shared__ __attribute__((aligned(16))) char smem[kAbsorbLds];   // either half's LDS
   const int bid = blockIdx.x;
   if (bid < n_abs) {
-    absorb_bf16_block<OUT_BF16>(bid, (lds_char*)smem, q, wuk, out, n_tok, H, n_tb);
+    absorb_bf16_block<OUT_BF16>(bid, (lds_char*)smem, q, wuk, out, n_tok, H);
   } else {
     const int r = bid - n_abs, n_hb = (H + kRope64Heads - 1) / kRope64Heads;
     rope64_block<true>(r / n_hb, r % n_hb, (lds_char*)smem, q_rope, q_rot, pos, H, base, freq);
@@ -168,14 +201,13 @@ hipError_t launch_absorb(const void* q_nope, const void* w_uk, void* q_lat, int 
                          int out_bf16, int n_tok, int H, hipStream_t s) {
   if (n_tok == 0) return hipSuccess;
   if (in_bf16) {
-    const int n_tb = (n_tok + kTokTile - 1) / kTokTile;
-    const dim3 grid(kNumXcd * ((H + kNumXcd - 1) / kNumXcd) * 4 * n_tb);
+    const dim3 grid(kNumXcd * ((H + kNumXcd - 1) / kNumXcd) * 4);
     if (out_bf16)
       hipLaunchKernelGGL(absorb_bf16_kernel<true>, grid, dim3(kThreads), 0, s,
-                         (const uint16_t*)q_nope, (const uint16_t*)w_uk, q_lat, n_tok, H, n_tb);
+                         (const uint16_t*)q_nope, (const uint16_t*)w_uk, q_lat, n_tok, H);
     else
       hipLaunchKernelGGL(absorb_bf16_kernel<false>, grid, dim3(kThreads), 0, s,
-                         (const uint16_t*)q_nope, (const uint16_t*)w_uk, q_lat, n_tok, H, n_tb);
+                         (const uint16_t*)q_nope, (const uint16_t*)w_uk, q_lat, n_tok, H);
   } else {
     hipLaunchKernelGGL(absorb_f32_kernel, dim3(n_tok * H, kDc / kF32Dims), dim3(kThreads), 0, s,
                        (const float*)q_nope, (const float*)w_uk, (float*)q_lat, n_tok, H);
@@ -188,17 +220,16 @@ hipError_t launch_absorb_rope(const uint16_t* q_nope, const uint16_t* w_uk, void
                               const int32_t* pos, int n_tok, int H, double base,
                               const double* freq, hipStream_t s) {
   if (n_tok == 0) return hipSuccess;
-  const int n_tb = (n_tok + kTokTile - 1) / kTokTile;
-  const int n_abs = kNumXcd * ((H + kNumXcd - 1) / kNumXcd) * 4 * n_tb;
+  const int n_abs = kNumXcd * ((H + kNumXcd - 1) / kNumXcd) * 4;
   const int n_rope = n_tok * ((H + kRope64Heads - 1) / kRope64Heads);
   static_assert(kRope64Threads == kThreads, "one block size for both halves");
   const dim3 grid(n_abs + n_rope);
   if (out_bf16)
     hipLaunchKernelGGL(absorb_rope_kernel<true>, grid, dim3(kThreads), 0, s, q_nope, w_uk, q_lat,
-                       n_tok, H, n_tb, n_abs, q_rope, q_rot, pos, base, freq);
+                       n_tok, H, n_abs, q_rope, q_rot, pos, base, freq);
   else
     hipLaunchKernelGGL(absorb_rope_kernel<false>, grid, dim3(kThreads), 0, s, q_nope, w_uk, q_lat,
-                       n_tok, H, n_tb, n_abs, q_rope, q_rot, pos, base, freq);
+                       n_tok, H, n_abs, q_rope, q_rot, pos, base, freq);
   return hipGetLastError();
 }
 

@@ -26,64 +26,101 @@ __device__ __forceinline__ bf16x8_t load_row8(const void* base, size_t off, bool
   return r;
 }
 
-// One workgroup per (head h, 64 output dims, 32 tokens); wave w owns output
-// dims 64*jb + 16*w .. +15 for the 32 tokens (two 16-token MFMA tiles). All
-// of a wave's operand loads (its 16 W_UV rows and the 32 u rows) are issued
-// before its first MFMA. Workgroups are placed so that the blocks of one
-// head, which read the same u rows, share an XCD (and its L2).
-constexpr int kTokTile = 32;
+// One workgroup of 4 waves per (head h, 64 tokens, 128 / NJ output dims). The
+// block's u rows are staged once in LDS (as bf16, 16-byte chunk c of token t
+// at c ^ (t & 15), so the 16 tokens of an MFMA A fragment hit 16 distinct
+// bank groups); wave w holds the W_UV[h] rows of its 32 / NJ output dims in
+// registers (the MFMA B operand, contiguous along the latent axis in memory)
+// and multiplies them against all 64 tokens. NJ = 1 when there are enough
+// (head, token block) pairs to fill the device, else 2. Workgroups are placed
+// so that the blocks of one head share an XCD (and W_UV[h] in its L2).
+constexpr int kTokTile = 64;
+constexpr int kUStage = kTokTile * kDc * 2;   // 64 KB
 
 // u row of (token n, head h) starts at n * u_tok + h * u_head elements:
 // (H * 512, 512) for per-head aggregates; (512, 0) for a latent shared by
-// every head (the key / value expansion of prefill).
-template <bool U_BF16, bool O_BF16>
+// every head.
+template <bool U_BF16, bool O_BF16, int NJ, int TT>
 __global__ __launch_bounds__(kThreads) void out_proj_bf16_kernel(const void* __restrict__ u,
                                                                  const uint16_t* __restrict__ wuv,
                                                                  void* __restrict__ o, int n_tok,
                                                                  int H, int n_tb, long u_tok,
                                                                  long u_head) {
+  constexpr int JB = 2 / NJ;                          // 16-wide output blocks per wave
+  __shared__ __attribute__((aligned(16))) char ush_raw[kUStage];
+  lds_char* const ush = (lds_char*)ush_raw;
   // blocks on XCD x (= blockIdx % 8) serve the heads h with h % 8 == x
   const int x = blockIdx.x % kNumXcd, idx = blockIdx.x / kNumXcd;
-  const int per_head = 2 * n_tb;
+  const int per_head = NJ * n_tb;
   const int h = kNumXcd * (idx / per_head) + x;
-  if (h >= H) return;
-  const int tb = (idx % per_head) >> 1, jb = idx & 1;
+  if (h >= H) return;                                 // uniform over the workgroup
+  const int tb = (idx % per_head) / NJ, jh = (idx % per_head) % NJ;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int i16 = lane & 15, G4 = lane >> 4;
-  const int j = 64 * jb + 16 * w + i16;               // this lane's output dim (B column)
-  const int n0 = tb * kTokTile;
+  const int j0 = (kDh / NJ) * jh + 16 * JB * w;       // this wave's first output dim
+  const int n0 = tb * kTokTile;                      // TT 16-token blocks from n0
 
-  bf16x8_t bw[16];
-  const uint16_t* wrow = wuv + ((size_t)h * kDh + j) * kDc + 8 * G4;
+  // the wave's W_UV rows, all in flight before the staging below waits
+  bf16x8_t bw[JB][16];
 #pragma unroll
-  for (int ks = 0; ks < 16; ++ks) bw[ks] = load_bf16x8(wrow + 32 * ks);
-  bf16x8_t a[2][16];
+  for (int jb = 0; jb < JB; ++jb) {
+    const uint16_t* wrow = wuv + ((size_t)h * kDh + j0 + 16 * jb + i16) * kDc + 8 * G4;
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    const int na = n0 + 16 * tt + i16;                // this lane's token (A row)
+    for (int ks = 0; ks < 16; ++ks) bw[jb][ks] = load_bf16x8(wrow + 32 * ks);
+  }
+  // stage u[n0 .. n0+16*TT-1][h][:] as bf16 (zero rows past n_tok): up to
+  // 16 chunks per thread, in rounds of at most 8 whose loads are all in
+  // flight before their first store
+  constexpr int kChunks = TT * 16 * kDc * 2 / 16 / kThreads;
+  constexpr int kRound = kChunks < 8 ? kChunks : 8;
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) {
-      a[tt][ks] = (bf16x8_t){0, 0, 0, 0, 0, 0, 0, 0};
-      if (na < n_tok)
-        a[tt][ks] = load_row8(u, (size_t)na * u_tok + (size_t)h * u_head + 32 * ks + 8 * G4, U_BF16);
+  for (int q0 = 0; q0 < kChunks; q0 += kRound) {
+    bf16x8_t uv[kRound];
+#pragma unroll
+    for (int q = 0; q < kRound; ++q) {
+      const int e = tid + kThreads * (q0 + q), t = e >> 6, c = e & 63;
+      const int n = n0 + t;
+      uv[q] = (bf16x8_t){0, 0, 0, 0, 0, 0, 0, 0};
+      if (n < n_tok) uv[q] = load_row8(u, (size_t)n * u_tok + (size_t)h * u_head + 8 * c, U_BF16);
+    }
+#pragma unroll
+    for (int q = 0; q < kRound; ++q) {
+      const int e = tid + kThreads * (q0 + q), t = e >> 6, c = e & 63;
+      *(MLA_LDS bf16x8_t*)(ush + t * (kDc * 2) + ((c & ~15) | ((c ^ t) & 15)) * 16) = uv[q];
     }
   }
-  f32x4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  __syncthreads();
+  f32x4_t acc[TT][JB];
 #pragma unroll
-  for (int ks = 0; ks < 16; ++ks)
+  for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) acc[tt] = mfma16x16x32(a[tt][ks], bw[ks], acc[tt]);
+    for (int jb = 0; jb < JB; ++jb) acc[tt][jb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt)
+  for (int ks = 0; ks < 16; ++ks) {
+    bf16x8_t a[TT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int n = n0 + 16 * tt + 4 * G4 + i;
-      if (n < n_tok) {
-        const size_t off = ((size_t)n * H + h) * kDh + j;
-        if (O_BF16) ((uint16_t*)o)[off] = f2bf(acc[tt][i]);
-        else ((float*)o)[off] = acc[tt][i];
-      }
+    for (int tt = 0; tt < TT; ++tt) {
+      const int t = 16 * tt + i16, c = 4 * ks + G4;
+      a[tt] = lds_read_b128(ush + t * (kDc * 2) + ((c & ~15) | ((c ^ t) & 15)) * 16);
     }
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+      for (int jb = 0; jb < JB; ++jb) acc[tt][jb] = mfma16x16x32(a[tt], bw[jb][ks], acc[tt][jb]);
+  }
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+    for (int jb = 0; jb < JB; ++jb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int n = n0 + 16 * tt + 4 * G4 + i;
+        if (n < n_tok) {
+          const size_t off = ((size_t)n * H + h) * kDh + j0 + 16 * jb + i16;
+          if (O_BF16) ((uint16_t*)o)[off] = f2bf(acc[tt][jb][i]);
+          else ((float*)o)[off] = acc[tt][jb][i];
+        }
+      }
 }
 
 // fp32: one workgroup of 4 waves per (token, head, 32 outputs); wave w
@@ -138,20 +175,40 @@ hipError_t launch_out_proj_strided(const void* u, long u_tok, long u_head, const
   if (n_tok == 0) return hipSuccess;
   if (w_bf16) {
     const int n_tb = (n_tok + kTokTile - 1) / kTokTile;
-    const dim3 grid(kNumXcd * ((H + kNumXcd - 1) / kNumXcd) * 2 * n_tb);
+    const int heads = kNumXcd * ((H + kNumXcd - 1) / kNumXcd);
+    // one block per (head, token block) when that fills the device, else two;
+    // a single short token block computes only its live 16-token blocks
+    const bool split_j = (int64_t)heads * n_tb < 256;
+    const int tt = n_tb > 1 ? 4 : (n_tok <= 16 ? 1 : n_tok <= 32 ? 2 : 4);
+    const dim3 grid(heads * n_tb * (split_j ? 2 : 1));
     const uint16_t* w = (const uint16_t*)w_uv;
-    if (u_bf16 && o_bf16)
-      hipLaunchKernelGGL((out_proj_bf16_kernel<true, true>), grid, dim3(kThreads), 0, s, u, w, o, n_tok, H, n_tb,
-                         u_tok, u_head);
-    else if (u_bf16)
-      hipLaunchKernelGGL((out_proj_bf16_kernel<true, false>), grid, dim3(kThreads), 0, s, u, w, o, n_tok, H, n_tb,
-                         u_tok, u_head);
-    else if (o_bf16)
-      hipLaunchKernelGGL((out_proj_bf16_kernel<false, true>), grid, dim3(kThreads), 0, s, u, w, o, n_tok, H, n_tb,
-                         u_tok, u_head);
-    else
-      hipLaunchKernelGGL((out_proj_bf16_kernel<false, false>), grid, dim3(kThreads), 0, s, u, w, o, n_tok, H, n_tb,
-                         u_tok, u_head);
+#define MLA_OUTP_T(UB, OB, NJ)                                                                \
+  if (tt == 1)                                                                                \
+    hipLaunchKernelGGL((out_proj_bf16_kernel<UB, OB, NJ, 1>), grid, dim3(kThreads), 0, s, u, w, \
+                       o, n_tok, H, n_tb, u_tok, u_head);                                     \
+  else if (tt == 2)                                                                           \
+    hipLaunchKernelGGL((out_proj_bf16_kernel<UB, OB, NJ, 2>), grid, dim3(kThreads), 0, s, u, w, \
+                       o, n_tok, H, n_tb, u_tok, u_head);                                     \
+  else                                                                                        \
+    hipLaunchKernelGGL((out_proj_bf16_kernel<UB, OB, NJ, 4>), grid, dim3(kThreads), 0, s, u, w, \
+                       o, n_tok, H, n_tb, u_tok, u_head);
+#define MLA_OUTP(UB, OB)  \
+  if (split_j) {          \
+    MLA_OUTP_T(UB, OB, 2) \
+  } else {                \
+    MLA_OUTP_T(UB, OB, 1) \
+  }
+    if (u_bf16 && o_bf16) {
+      MLA_OUTP(true, true)
+    } else if (u_bf16) {
+      MLA_OUTP(true, false)
+    } else if (o_bf16) {
+      MLA_OUTP(false, true)
+    } else {
+      MLA_OUTP(false, false)
+    }
+#undef MLA_OUTP
+#undef MLA_OUTP_T
   } else {
     hipLaunchKernelGGL(out_proj_f32_kernel, dim3(n_tok * H, kF32Blocks), dim3(64 * kF32Waves), 0, s,
                        (const float*)u, (const float*)w_uv, (float*)o, H, u_tok, u_head);
