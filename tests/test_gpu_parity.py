@@ -81,8 +81,12 @@ def test_rope_parity_long_positions(mla, dt, H, dr):
     assert np.array_equal(y, y2)
 
 
-@pytest.mark.parametrize("dt,n_tok,H", [("f32", 1, 16), ("bf16", 32, 128), ("bf16", 300, 16)])
+@pytest.mark.parametrize("dt,n_tok,H", [("f32", 1, 16), ("bf16", 32, 128), ("bf16", 300, 16),
+                                        ("bf16", 256, 128), ("bf16", 7, 24)])
 def test_absorb_and_out_proj_parity(mla, dt, n_tok, H):
+    # bf16 token counts cover: one token block and several with a ragged tail
+    # (absorb walks 32-token blocks), out_proj with one and two workgroups per
+    # (head, 64-token block), and a single short block of 16 or 32 tokens
     rng = np.random.default_rng(n_tok)
     q = synth.store(rng.standard_normal((n_tok, H, 128)), dt)
     w = synth.store(rng.standard_normal((H, 128, 512)) / np.sqrt(512), dt)
@@ -93,6 +97,16 @@ def test_absorb_and_out_proj_parity(mla, dt, n_tok, H):
     o = host(mla.out_proj(mla.to_device(u, dt), mla.to_device(w, dt), out_dtype=torch.float32))
     ref_o = O.out_proj(O.stored_to_f64(u, dt), O.stored_to_f64(w, dt))
     assert row_rel(o, ref_o) <= (1e-5 if dt == "f32" else 1e-5 * 8)
+
+
+def test_out_proj_f32_u_with_bf16_weights(mla):
+    """fp32 aggregates against bf16 W_UV: u is rounded to bf16 for the MFMA."""
+    rng = np.random.default_rng(5)
+    u = synth.store(rng.standard_normal((100, 16, 512)), "f32")
+    w = synth.store(rng.standard_normal((16, 128, 512)) / np.sqrt(512), "bf16")
+    o = host(mla.out_proj(mla.to_device(u, "f32"), mla.to_device(w, "bf16"), out_dtype=torch.float32))
+    ref_o = O.out_proj(O.stored_to_f64(u, "f32"), O.stored_to_f64(w, "bf16"))
+    assert row_rel(o, ref_o) <= 8e-3
 
 
 # --------------------------------------------------------------------------
