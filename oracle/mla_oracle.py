@@ -39,7 +39,8 @@ analysis"):
 
 Pins that tie this oracle to something other than itself live in
 tests/test_oracle_pins.py. Parity unpinned: nothing here models the GPU
-path's internal bf16/fp8 rounding of q_lat or of softmax weights.
+path's internal bf16/fp8 rounding of q_lat, of softmax weights or of split
+partials.
 """
 from __future__ import annotations
 
