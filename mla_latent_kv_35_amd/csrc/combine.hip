@@ -281,30 +281,40 @@ __global__ __launch_bounds__(64 * kWaveRows) void combine_wave_kernel(CombinePar
 // for both), writes u and lse, and stages u as bf16 in LDS; after one
 // barrier it computes its 16 x 16 block of o = u W_UV[h]^T on MFMA with the
 // same operands and k order as out_proj, so o equals combine followed by
-// out_proj bit for bit.
+// out_proj bit for bit. When (head, token block) pairs alone would leave CUs
+// idle, each pair gets two workgroups that split the output dims (waves 0-3
+// project 64 of them; both merge the same rows and the first writes u).
 constexpr int kOutTok = 16;
 constexpr int kOutThreads = 512;
 constexpr int kUPitch = kDc * 2 + 16;   // bf16 row + 16 B: rows start 4 banks apart
 
-__global__ __launch_bounds__(kOutThreads) void combine_out_kernel(CombineParams p, int n_rb) {
+__global__ __launch_bounds__(kOutThreads) void combine_out_kernel(CombineParams p, int n_rb, int nj) {
   __shared__ __attribute__((aligned(16))) char ush_raw[kOutTok * kUPitch];
   lds_char* const ush = (lds_char*)ush_raw;
   // the row blocks of one head run on one XCD (they read the same W_UV[h])
-  int h, rb;
+  int h, r2;
   if (p.H % kNumXcd == 0) {
-    h = (blockIdx.x / (kNumXcd * n_rb)) * kNumXcd + blockIdx.x % kNumXcd;
-    rb = (blockIdx.x / kNumXcd) % n_rb;
+    h = (blockIdx.x / (kNumXcd * n_rb * nj)) * kNumXcd + blockIdx.x % kNumXcd;
+    r2 = (blockIdx.x / kNumXcd) % (n_rb * nj);
   } else {
-    h = blockIdx.x / n_rb;
-    rb = blockIdx.x % n_rb;
+    h = blockIdx.x / (n_rb * nj);
+    r2 = blockIdx.x % (n_rb * nj);
   }
   if (h >= p.H) return;                            // uniform over the workgroup
+  const int rb = r2 / nj, jh = r2 % nj;            // token block, output-dim half
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int i16 = lane & 15, G4 = lane >> 4;
+  // output dims of this wave: 16 of 128, or (two workgroups per pair) waves
+  // 0-3 take 16 of this workgroup's 64
+  const bool projects = nj == 1 || wv < 4;         // wave-uniform
+  const int jw = nj == 1 ? 16 * wv : 64 * jh + 16 * wv;
   bf16x8_t wf[16];
-  const uint16_t* wrow = p.w_uv + ((size_t)h * kDh + 16 * wv + i16) * kDc + 8 * G4;
+  if (projects) {
+    const uint16_t* wrow = p.w_uv + ((size_t)h * kDh + jw + i16) * kDc + 8 * G4;
 #pragma unroll
-  for (int ks = 0; ks < 16; ++ks) wf[ks] = load_bf16x8(wrow + 32 * ks);
+    for (int ks = 0; ks < 16; ++ks) wf[ks] = load_bf16x8(wrow + 32 * ks);
+  }
+  const bool writes_u = p.out != nullptr && jh == 0;
   const int n0 = kOutTok * rb + 2 * wv;            // this wave's two tokens
   u32x4_t packed[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
   if (n0 + 1 < p.n_tok) {                          // wave-uniform
@@ -315,7 +325,7 @@ __global__ __launch_bounds__(kOutThreads) void combine_out_kernel(CombineParams 
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) packed[t][i] = pack_bf16x2(u[t][2 * i], u[t][2 * i + 1]);
-      if (p.out) store_u_row(p, rows[t], lane, u[t], lse[t]);
+      if (writes_u) store_u_row(p, rows[t], lane, u[t], lse[t]);
     }
   } else if (n0 < p.n_tok) {
     const int rows[1] = {n0 * p.H + h};
@@ -323,12 +333,13 @@ __global__ __launch_bounds__(kOutThreads) void combine_out_kernel(CombineParams 
     combine_rows_any<1>(p, rows, lane, u, lse);
 #pragma unroll
     for (int i = 0; i < 4; ++i) packed[0][i] = pack_bf16x2(u[0][2 * i], u[0][2 * i + 1]);
-    if (p.out) store_u_row(p, rows[0], lane, u[0], lse[0]);
+    if (writes_u) store_u_row(p, rows[0], lane, u[0], lse[0]);
   }
 #pragma unroll
   for (int t = 0; t < 2; ++t)
     *(MLA_LDS u32x4_t*)(ush + (2 * wv + t) * kUPitch + lane * 16) = packed[t];
   __syncthreads();
+  if (!projects) return;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ks = 0; ks < 16; ++ks)
@@ -337,7 +348,7 @@ __global__ __launch_bounds__(kOutThreads) void combine_out_kernel(CombineParams 
   for (int i = 0; i < 4; ++i) {
     const int n = kOutTok * rb + 4 * G4 + i;
     if (n < p.n_tok) {
-      const size_t off = ((size_t)n * p.H + h) * kDh + 16 * wv + i16;
+      const size_t off = ((size_t)n * p.H + h) * kDh + jw + i16;
       if (p.o_bf16) ((uint16_t*)p.o)[off] = f2bf(acc[i]);
       else ((float*)p.o)[off] = acc[i];
     }
@@ -349,7 +360,9 @@ __global__ __launch_bounds__(kOutThreads) void combine_out_kernel(CombineParams 
 hipError_t launch_combine_out(const CombineParams& p, hipStream_t s) {
   if (p.n_split > 64 || !p.w_uv || !p.o) return hipErrorInvalidValue;
   const int n_rb = (p.n_tok + kOutTok - 1) / kOutTok;
-  hipLaunchKernelGGL(combine_out_kernel, dim3(p.H * n_rb), dim3(kOutThreads), 0, s, p, n_rb);
+  const int nj = (int64_t)p.H * n_rb < 256 ? 2 : 1;   // split the output dims to fill the CUs
+  hipLaunchKernelGGL(combine_out_kernel, dim3(p.H * n_rb * nj), dim3(kOutThreads), 0, s, p, n_rb,
+                     nj);
   return hipGetLastError();
 }
 
