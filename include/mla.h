@@ -109,8 +109,9 @@ int mla_rope_freq(const void* x_in, void* x_out, int dt, const int32_t* pos,
  * mla_rope_freq(..., theta) when theta is not NULL -- bit for bit. The two
  * halves of the V2 analysis page's query (section 1.3, eq. 14-15: the
  * absorbed content part and the separately rotated rope part) are
- * independent, so with BF16 queries, BF16 rope data, d_r = 64 and 16-byte
- * aligned rope rows they run as one kernel launch; otherwise as the two calls.
+ * independent, so with queries and rope data both BF16 or both F32, d_r = 64
+ * and 16-byte aligned rope rows they run as one kernel launch; otherwise as
+ * the two calls.
  *   q_nope, w_uk, q_lat, q_dt, out_dt, d_h, d_c : as mla_absorb_q (n_tok x H)
  *   q_rope, q_rot : [n_tok][H][d_r], dtype rope_dt (F32 or BF16); may alias
  *   pos           : int32 [n_tok]

@@ -170,15 +170,14 @@ __global__ __launch_bounds__(kThreads) void absorb_rope_kernel(
 // W_UK[h]), then the four partial sums are added in a fixed order.
 constexpr int kF32Dims = 256;
 
-__global__ __launch_bounds__(kThreads) void absorb_f32_kernel(const float* __restrict__ q,
-                                                              const float* __restrict__ wuk,
-                                                              float* __restrict__ out, int n_tok,
-                                                              int H) {
-  __shared__ float part[kThreads / 64][kF32Dims];
-  const int nh = blockIdx.x;          // n*H + h
+// part: kThreads / 64 x kF32Dims floats of LDS for the partial sums
+__device__ __forceinline__ void absorb_f32_block(int nh, int y, float* part,
+                                                 const float* __restrict__ q,
+                                                 const float* __restrict__ wuk,
+                                                 float* __restrict__ out, int H) {
   const int h = nh % H;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int d0 = blockIdx.y * kF32Dims;
+  const int d0 = y * kF32Dims;
   const float* qr = q + (size_t)nh * kDh + 32 * w;
   const float* wh = wuk + ((size_t)h * kDh + 32 * w) * kDc + d0;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
@@ -189,10 +188,36 @@ __global__ __launch_bounds__(kThreads) void absorb_f32_kernel(const float* __res
     for (int i = 0; i < 4; ++i) acc[i] = fmaf(qj, wh[(size_t)j * kDc + lane + 64 * i], acc[i]);
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) part[w][lane + 64 * i] = acc[i];
+  for (int i = 0; i < 4; ++i) part[w * kF32Dims + lane + 64 * i] = acc[i];
   __syncthreads();
   const int d = threadIdx.x;
-  out[(size_t)nh * kDc + d0 + d] = ((part[0][d] + part[1][d]) + part[2][d]) + part[3][d];
+  out[(size_t)nh * kDc + d0 + d] =
+      ((part[d] + part[kF32Dims + d]) + part[2 * kF32Dims + d]) + part[3 * kF32Dims + d];
+}
+
+__global__ __launch_bounds__(kThreads) void absorb_f32_kernel(const float* __restrict__ q,
+                                                              const float* __restrict__ wuk,
+                                                              float* __restrict__ out, int n_tok,
+                                                              int H) {
+  __shared__ float part[kThreads / 64 * kF32Dims];
+  absorb_f32_block(blockIdx.x, blockIdx.y, part, q, wuk, out, H);
+}
+
+// fp32 query side in one launch: block 2*(n*H + h) + y absorbs as
+// absorb_f32_kernel's block (n*H + h, y) does, the rest rotate as the fp32
+// d_r = 64 rope kernel does; the two halves touch disjoint buffers.
+__global__ __launch_bounds__(kThreads) void absorb_rope_f32_kernel(
+    const float* __restrict__ q, const float* __restrict__ wuk, float* __restrict__ out, int H,
+    int n_abs, const float* q_rope, float* q_rot, const int32_t* pos, double base,
+    const double* freq) {
+  __shared__ __attribute__((aligned(16))) float part[kThreads / 64 * kF32Dims];   // either half's LDS
+  const int bid = blockIdx.x;
+  if (bid < n_abs) {
+    absorb_f32_block(bid >> 1, bid & 1, part, q, wuk, out, H);
+  } else {
+    const int r = bid - n_abs, n_hb = (H + kRope64Heads - 1) / kRope64Heads;
+    rope64_block<false>(r / n_hb, r % n_hb, (lds_char*)part, q_rope, q_rot, pos, H, base, freq);
+  }
 }
 
 }  // namespace
@@ -230,6 +255,23 @@ hipError_t launch_absorb_rope(const uint16_t* q_nope, const uint16_t* w_uk, void
   else
     hipLaunchKernelGGL(absorb_rope_kernel<false>, grid, dim3(kThreads), 0, s, q_nope, w_uk, q_lat,
                        n_tok, H, n_abs, q_rope, q_rot, pos, base, freq);
+  return hipGetLastError();
+}
+
+}  // namespace mla
+
+namespace mla {
+
+hipError_t launch_absorb_rope_f32(const float* q_nope, const float* w_uk, float* q_lat,
+                                  const float* q_rope, float* q_rot, const int32_t* pos, int n_tok,
+                                  int H, double base, const double* freq, hipStream_t s) {
+  if (n_tok == 0) return hipSuccess;
+  static_assert(kRope64Threads == kThreads, "one block size for both halves");
+  static_assert(kThreads / 64 * kF32Dims * 4 >= 512, "the rope (cos, sin) table fits");
+  const int n_abs = n_tok * H * (kDc / kF32Dims);
+  const int n_rope = n_tok * ((H + kRope64Heads - 1) / kRope64Heads);
+  hipLaunchKernelGGL(absorb_rope_f32_kernel, dim3(n_abs + n_rope), dim3(kThreads), 0, s, q_nope,
+                     w_uk, q_lat, H, n_abs, q_rope, q_rot, pos, base, freq);
   return hipGetLastError();
 }
 

@@ -175,6 +175,11 @@ int mla_absorb_q_rope(const void* q_nope, const void* w_uk, void* q_lat, int q_d
     e = launch_absorb_rope((const uint16_t*)q_nope, (const uint16_t*)w_uk, q_lat,
                            out_dt == MLA_BF16, (const uint16_t*)q_rope, (uint16_t*)q_rot, pos,
                            n_tok, H, theta ? 1.0 : base, theta, s);
+  } else if (q_dt == MLA_F32 && rope_dt == MLA_F32 && d_r == 64 &&
+             (((uintptr_t)q_rope | (uintptr_t)q_rot) & 15) == 0) {
+    e = launch_absorb_rope_f32((const float*)q_nope, (const float*)w_uk, (float*)q_lat,
+                               (const float*)q_rope, (float*)q_rot, pos, n_tok, H,
+                               theta ? 1.0 : base, theta, s);
   } else {
     e = launch_absorb(q_nope, w_uk, q_lat, q_dt == MLA_BF16, out_dt == MLA_BF16, n_tok, H, s);
     if (e == hipSuccess)

@@ -50,5 +50,9 @@ hipError_t launch_absorb_rope(const uint16_t* q_nope, const uint16_t* w_uk, void
                               int out_bf16, const uint16_t* q_rope, uint16_t* q_rot,
                               const int32_t* pos, int n_tok, int H, double base,
                               const double* freq, hipStream_t s);
+// the same for fp32 queries, W_UK, q_lat and rope data
+hipError_t launch_absorb_rope_f32(const float* q_nope, const float* w_uk, float* q_lat,
+                                  const float* q_rope, float* q_rot, const int32_t* pos, int n_tok,
+                                  int H, double base, const double* freq, hipStream_t s);
 
 }  // namespace mla

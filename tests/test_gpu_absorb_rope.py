@@ -25,7 +25,9 @@ CASES = [
     (70, 16, "bf16", "bf16", "bf16", 64, False),      # three token tiles, ragged tail
     (5, 40, "bf16", "f32", "bf16", 64, True),         # H not a multiple of 8 or 32; YaRN
     (3, 8, "bf16", "bf16", "f32", 64, False),         # fp32 rope data: two launches
-    (9, 16, "f32", "f32", "f32", 64, False),          # fp32 queries: two launches
+    (9, 16, "f32", "f32", "f32", 64, False),          # fp32 queries and rope: one launch
+    (6, 40, "f32", "f32", "f32", 64, True),           # the same with H % 32 != 0 and YaRN
+    (4, 16, "f32", "f32", "bf16", 64, False),         # fp32 queries, bf16 rope: two launches
     (4, 16, "bf16", "bf16", "bf16", 32, False),       # d_r != 64: two launches
     (1, 1, "bf16", "bf16", "bf16", 64, False),        # one token, one head
 ]
