@@ -25,6 +25,8 @@ CASES = [
     dict(B=1, H=16, T=1, seq_len=900, ragged=False, split=64),                    # 1 token, 15 splits
     dict(B=17, H=64, T=1, seq_len=200, ragged=True, split=64),                    # 17 tokens: 2 blocks
     dict(B=4, H=128, T=2, seq_len=300, ragged=False, ckv_dt="fp8", split=128),
+    dict(B=3, H=40, T=1, seq_len=250, ragged=True, split=64),                     # H % 8 != 0
+    dict(B=40, H=128, T=1, seq_len=130, ragged=False, split=64),                  # 3 token blocks
 ]
 
 
