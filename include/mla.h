@@ -201,8 +201,9 @@ typedef struct mla_decode_args {
   /* Optional value up-projection in the same call (V2 analysis page,
    * section 6.1: each head aggregates first, then applies its own matrix):
    * o[b][t][h][:] = W_UV[h] u[b][t][h][:], exactly as mla_out_proj computes
-   * it from u. With more than one split and bf16 weights the log-sum-exp
-   * combine and the projection run as one kernel (u is still written). */
+   * it from u. With 2 to 4 splits and bf16 weights the log-sum-exp combine
+   * and the projection run as one kernel (u is still written); otherwise as
+   * the combine followed by the projection, with the same results. */
   const void* w_uv;         /* [H][128][d_c] dtype w_dt, or NULL: no projection */
   int32_t w_dt;             /* BF16, or F32 with F32 u and o (fp32 pools) */
   int32_t o_dt;             /* F32 or BF16 */

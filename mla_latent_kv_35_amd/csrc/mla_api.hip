@@ -292,7 +292,9 @@ int mla_decode_paged(const mla_decode_args* a, void* stream) {
     c.max_seq_len = a->max_seq_len;
     c.max_pages = a->max_pages_per_seq;
     c.out_bf16 = p.out_bf16;
-    if (proj && a->w_dt == MLA_BF16 && pl.n_split <= 64) {
+    // the fused combine + projection measured faster with up to 4 splits and
+    // slower with 16 or 32 (its workgroups hold W_UV while they merge)
+    if (proj && a->w_dt == MLA_BF16 && pl.n_split <= 4) {
       c.w_uv = (const uint16_t*)a->w_uv;
       c.o = a->o;
       c.o_bf16 = a->o_dt == MLA_BF16;

@@ -20,13 +20,16 @@ def bits(t):
 
 
 CASES = [
-    dict(B=3, H=128, T=1, seq_len=700, ragged=True, permuted=True, split=128),
-    dict(B=5, H=32, T=2, seq_len=333, ragged=True, permuted=True, split=64),      # 10 tokens
-    dict(B=1, H=16, T=1, seq_len=900, ragged=False, split=64),                    # 1 token, 15 splits
+    # the fused kernel runs with 2-4 splits; more splits take the combine and
+    # out_proj separately (the last case)
+    dict(B=3, H=128, T=1, seq_len=700, ragged=True, permuted=True, split=192),
+    dict(B=5, H=32, T=2, seq_len=333, ragged=True, permuted=True, split=128),     # 10 tokens
+    dict(B=1, H=16, T=1, seq_len=900, ragged=False, split=256),                   # 1 token, 4 splits
     dict(B=17, H=64, T=1, seq_len=200, ragged=True, split=64),                    # 17 tokens: 2 blocks
     dict(B=4, H=128, T=2, seq_len=300, ragged=False, ckv_dt="fp8", split=128),
     dict(B=3, H=40, T=1, seq_len=250, ragged=True, split=64),                     # H % 8 != 0
     dict(B=40, H=128, T=1, seq_len=130, ragged=False, split=64),                  # 3 token blocks
+    dict(B=1, H=16, T=1, seq_len=900, ragged=False, split=64),                    # 15 splits
 ]
 
 
@@ -52,7 +55,7 @@ def test_fused_projection_f32_output_and_no_split(mla):
     d = mla.upload(inp)
     q_lat = mla.absorb_q(d.q_nope, d.w_uk)
     q_rot = mla.rope(d.q_rope, d.positions)
-    for split in (64, 448):                    # several splits (fused), then one (separate launch)
+    for split in (128, 448):                   # 4 splits (fused), then one (separate launch)
         o32 = torch.empty((6, 32, 128), dtype=torch.float32, device="cuda")
         u, lse, o = mla.decode_paged(q_lat, q_rot, d.cache, 1, cfg.softmax_scale,
                                      split_tokens=split, w_uv=d.w_uv, o=o32)
@@ -66,7 +69,7 @@ def test_fused_projection_of_bad_sequence_is_nan(mla):
     inp = synth.make_inputs(cfg)
     d = mla.upload(inp)
     d.cache.seq_lens[1] = d.cache.max_seq_len + 5
-    out = mla.decode_step(d, split_tokens=64, fused=True)
+    out = mla.decode_step(d, split_tokens=128, fused=True)   # 3 splits: the fused kernel
     torch.cuda.synchronize()
     o = out["o"].float().cpu().numpy()
     assert np.isnan(o[1]).all() and not np.isnan(o[[0, 2]]).any()
