@@ -10,6 +10,7 @@ namespace mla {
 namespace {
 
 constexpr int kNumCu = 256;           // MI355X compute units
+constexpr int kMaxSplits = 1024;      // splits per sequence the combine kernel merges
 constexpr size_t kWsAlign = 256;
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -19,7 +20,8 @@ bool is_float_dt(int dt) { return dt == MLA_F32 || dt == MLA_BF16; }
 struct Plan {
   int split_tokens = 0;
   int n_split = 1;
-  int G = 1;              // 64-row groups (MFMA kernels)
+  int rows = kRowsPerGroup;  // query rows per workgroup (MFMA kernels: 64 or 128)
+  int G = 1;              // row groups per sequence (MFMA kernels)
   size_t part_u_bytes = 0;
   size_t ws_bytes = 0;
 };
@@ -64,7 +66,11 @@ Plan make_plan(const mla_decode_args* a) {
   const int64_t total = a->total_tokens > 0 ? a->total_tokens : (int64_t)a->B * Lmax;
   const int64_t pages_total = (total + kPage - 1) / kPage;
   const int64_t max_pages = (Lmax + kPage - 1) / kPage;
-  pl.G = (int)((R + kRowsPerGroup - 1) / kRowsPerGroup);
+  // 128 rows per workgroup when the batch's row groups alone fill the GPU
+  // (each page is then read by one workgroup); else 64, whose two row groups
+  // of a sequence share every page through L2
+  if (a->ckv_dt != MLA_F32 && (int64_t)a->B * ((R + 127) / 128) >= kNumCu) pl.rows = 128;
+  pl.G = (int)((R + pl.rows - 1) / pl.rows);
   if (a->split_tokens > 0) {
     pl.split_tokens = a->split_tokens;
   } else if (a->ckv_dt == MLA_F32) {
@@ -216,6 +222,7 @@ int mla_decode_plan(const mla_decode_args* args, int* split_tokens, int* n_split
   const int st = check_shape(args);
   if (st != MLA_OK) return st;
   const Plan pl = make_plan(args);
+  if (pl.n_split > kMaxSplits) return MLA_ERR_UNSUPPORTED;
   if (split_tokens) *split_tokens = pl.split_tokens;
   if (n_split) *n_split = pl.n_split;
   if (workspace_bytes) *workspace_bytes = pl.ws_bytes;
@@ -234,7 +241,14 @@ int mla_decode_paged(const mla_decode_args* a, void* stream) {
     if (!is_float_dt(a->w_dt) || !is_float_dt(a->o_dt)) return MLA_ERR_DTYPE;
     if (a->w_dt == MLA_F32 && (a->out_dt != MLA_F32 || a->o_dt != MLA_F32)) return MLA_ERR_DTYPE;
   }
+  // every vector access of the decode kernels is 16 bytes wide
+  const uintptr_t al = (uintptr_t)a->q_lat | (uintptr_t)a->q_rope | (uintptr_t)a->ckv |
+                       (uintptr_t)a->kr | (uintptr_t)a->out |
+                       (proj ? ((uintptr_t)a->w_uv | (uintptr_t)a->o) : 0);
+  if (al % 16 != 0 || (uintptr_t)a->ckv_scale % 4 != 0 || (uintptr_t)a->lse % 4 != 0)
+    return MLA_ERR_UNSUPPORTED;
   const Plan pl = make_plan(a);
+  if (pl.n_split > kMaxSplits) return MLA_ERR_UNSUPPORTED;
   if (pl.n_split > 1) {
     if (!a->workspace || a->workspace_bytes < pl.ws_bytes) return MLA_ERR_WORKSPACE;
     if (((uintptr_t)a->workspace) % kWsAlign != 0) return MLA_ERR_WORKSPACE;
@@ -273,8 +287,8 @@ int mla_decode_paged(const mla_decode_args* a, void* stream) {
   const hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if (a->ckv_dt == MLA_F32) e = launch_decode_simple_f32(p, s);
-  else if (a->ckv_dt == MLA_BF16) e = launch_decode_mfma_bf16(p, s);
-  else e = launch_decode_mfma_fp8(p, s);
+  else if (a->ckv_dt == MLA_BF16) e = launch_decode_split(p, 0, pl.rows, s);
+  else e = launch_decode_split(p, 1, pl.rows, s);
   if (e != hipSuccess) return MLA_ERR_LAUNCH;
   if (pl.n_split > 1) {
     CombineParams c{};
