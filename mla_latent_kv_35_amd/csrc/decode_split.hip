@@ -55,6 +55,7 @@ constexpr int kThreads = 256;
 constexpr int kTile = 32;
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 template <bool FP8>
 struct Geo {
@@ -65,7 +66,6 @@ struct Geo {
   static constexpr int kTileBytes = kScaleOff + (FP8 ? 256 : 0);
   static constexpr int kNumBuf = FP8 ? 6 : 4;
   static constexpr int kLatCopies = FP8 ? 16 : 32;        // 1-KB copies per tile
-  static constexpr int kCopies = kLatCopies + 4 + (FP8 ? 1 : 0);
   static constexpr int kOffIds = kNumBuf * kTileBytes;
   static constexpr int kTilesEnd = kOffIds + kMaxSplitPages * 4;
   // end of the unit: U halves of the four waves ([wave][8 blocks][lane] x 64 B)
@@ -93,15 +93,6 @@ __device__ __forceinline__ int fsw(int t) {
   return (t & 8) | ((t & 2) << 1) | ((t & 1) << 1) | ((t >> 2) & 1);
 }
 __device__ __forceinline__ int swz_rope(int t) { return (t >> 1) & 7; }
-
-// A wave-uniform pointer, in scalar registers (the copy instructions take
-// their base address there).
-__device__ __forceinline__ const char* uniform_ptr(const char* q) {
-  const uint64_t v = (uint64_t)q;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return (const char*)(((uint64_t)hi << 32) | lo);
-}
 
 // Wait until at most N of this wave's vector-memory operations are in flight
 // (6-bit vmcnt of gfx9: bits 3:0 and 15:14).
@@ -190,7 +181,6 @@ void decode_split_kernel(DecodeParams p) {
   constexpr int LA = NB / NT - 1;            // copy lookahead in steps
   constexpr int kLatRow = Gm::kLatRow;
   constexpr int kTileBytes = Gm::kTileBytes;
-  constexpr int kCopies = Gm::kCopies;
   static_assert(NRB * NT == 4 && LA >= 1, "geometry");
   __shared__ __attribute__((aligned(16))) char smem_raw[Gm::kLdsBytes];
   lds_char* const smem = (lds_char*)smem_raw;
@@ -206,6 +196,7 @@ void decode_split_kernel(DecodeParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  __builtin_assume(w >= 0 && w < kThreads / 64);
   const int rbw = w % NRB;                   // the wave's 32-row block
   const int th = w / NRB;                    // the wave's tile parity
 
@@ -285,8 +276,8 @@ void decode_split_kernel(DecodeParams p) {
     int lane, t32, h;
     int lat_sw, rope_sw;                        // score reads of token t32
     int tr_base;                                // bf16 transposed reads: row of token 4h + i/4
-    uint32_t lat_off0, lat_off1, rope_off;      // copy source offsets
-    int tl8, rope_t;
+    uint32_t cv[4];                             // per-lane copy source offsets (see copy_op)
+    uint32_t rope_v;
   };
   auto lanes_now = [&]() __attribute__((always_inline)) -> Lanes {
     int ln = lane;
@@ -298,92 +289,115 @@ void decode_split_kernel(DecodeParams p) {
     o.lat_sw = FP8 ? fsw(o.t32) : gsw(o.t32);
     o.rope_sw = swz_rope(o.t32);
     o.tr_base = (4 * o.h + ((ln & 15) >> 2)) * kLatRow;
-    // copy ops: bf16 latent row t = w + 4 op takes chunk lane ^ gsw(t),
-    // gsw(t) = 4w + (op & 3) (lat_off0 holds lane ^ 4w); fp8 latent rows
-    // t = tl8 + 8 op (a pair per instruction) take chunk (lane & 31) ^ fsw(t),
-    // two values by op parity; the rope block of wave w holds tokens
-    // 8w + lane / 8
-    o.lat_off0 = FP8 ? (uint32_t)(((ln & 31) ^ fsw(2 * w + (ln >> 5))) * 16)
-                     : (uint32_t)(ln ^ (4 * w));
-    o.lat_off1 = FP8 ? (uint32_t)(((ln & 31) ^ fsw(2 * w + (ln >> 5) + 8)) * 16) : 0u;
-    o.tl8 = 2 * w + (ln >> 5);
-    o.rope_t = 8 * w + (ln >> 3);
-    o.rope_off = (uint32_t)(((ln & 7) ^ swz_rope(o.rope_t)) * 16);
+    // copy sources, relative to the first row of the wave's copy group (see
+    // copy_op): bf16 latent rows 4w + 16g + j hold chunk c at c ^ gsw, with
+    // gsw = 4j + w, so lane l fetches chunk l ^ (4j + w) of row j; fp8 row
+    // pair i of rows 8w + 2i + lane / 32 takes chunk (lane & 31) ^ fsw(t) of
+    // its row; rope tokens 8w + lane / 8 take chunk (lane & 7) ^ swz_rope(t)
+    if constexpr (!FP8) {
+#pragma clang loop unroll(full)
+      for (int j = 0; j < 4; ++j) o.cv[j] = (uint32_t)((ln ^ (4 * j + w)) << 4);
+    } else {
+#pragma clang loop unroll(full)
+      for (int i = 0; i < 4; ++i)
+        o.cv[i] = (uint32_t)((ln >> 5) * 512 + (((ln & 31) ^ fsw(8 * w + 2 * i + (ln >> 5))) << 4));
+    }
+    o.rope_v = (uint32_t)((ln >> 3) * 128 + (((ln & 7) ^ swz_rope(8 * w + (ln >> 3))) << 4));
     return o;
   };
 
   // ---- page copies ----------------------------------------------------------
   const char* const ckv_base = (const char*)p.ckv;
   const char* const kr_base = (const char*)p.kr;
-  // copy op `op` of tile jt by this wave: bf16 ops 0-7 latent rows, fp8 ops
-  // 0-3 latent row pairs, then the rope block (8 tokens), then (fp8, wave 0)
-  // the 32 token scales
-  auto copy_op = [&](const Lanes& ln, int jt, int id, int op) __attribute__((always_inline)) {
+  // one tile's sources (scalar): the page's pool rows, the tile's first slot
+  // in the page (0 or 32), the page's last valid slot (>= 0: a tile's page
+  // always holds a token of the sequence, even when the tile itself starts
+  // past the end) and the destination buffer
+  struct TileSrc {
+    const char* cp;
+    const char* rp;
+    const char* sp;
+    int lds, sb, last;
+    bool full;                                         // every slot holds a token
+  };
+  auto tile_src = [&](int jt, int id, int jdst) __attribute__((always_inline)) -> TileSrc {
     const int t0 = tok0 + jt * kTile;                  // first token of the tile
-    const int sb = t0 % kPage;                         // 0 or 32 within the page
-    const int last = L - 1 - (t0 - sb);                // last valid slot of the page
+    const int sb = t0 & (kPage - 1);
     const bool ok = id >= 0 && id < p.n_pages;
     const size_t idc = ok ? (size_t)id : 0;
-    lds_char* const tile = smem + (jt % NB) * kTileBytes;
-    constexpr int kLatOps = FP8 ? 4 : 8;
+    TileSrc ts;
+    ts.cp = ckv_base + idc * (kPage * kLatRow);
+    ts.rp = kr_base + idc * (kPage * kDr * 2);
+    ts.sp = FP8 ? (const char*)p.ckv_scale + idc * (kPage * 4) : nullptr;
+    ts.lds = (jdst % NB) * kTileBytes;
+    ts.sb = sb;
+    ts.last = min(L - 1 - (t0 - sb), kPage - 1);       // in [0, 63]
+    ts.full = sb + kTile - 1 <= ts.last;
+    return ts;
+  };
+  // copy op `op` of a tile by this wave, one 1-KB (or 128-byte) copy each:
+  //  bf16: ops 0-7 copy latent row 4w + 16 (op / 4) + op % 4, op 8 the rope
+  //        of tokens 8w..8w + 7;
+  //  fp8:  ops 0-3 copy latent rows 8w + 2 op, 8w + 2 op + 1, op 4 the rope,
+  //        op 5 the 32 token scales (every wave copies the same 128 bytes, so
+  //        all waves count the same number of copies).
+  // The copies of a row group share one global and one LDS base (the row's
+  // offset rides in the instruction). Slot sb + t reads page slot
+  // min(sb + t, last), in [0, 63]: a tile that reaches past the sequence end
+  // takes the per-row path.
+  constexpr int kLatOps = FP8 ? 4 : 8;
+  auto copy_op = [&](const Lanes& ln, const TileSrc& ts, int op) __attribute__((always_inline)) {
+    const lds_char* const dst = smem + ts.lds;
     if (op < kLatOps) {
-      const char* const cp = uniform_ptr(ckv_base + idc * (kPage * kLatRow));
-      if constexpr (!FP8) {
-        const int t = w + 4 * op;   // gsw(t) = 4w + (op & 3)
-        const int ts = min(sb + t, last);
-        dma_copy16(cp, (uint32_t)(ts * 1024) + ((ln.lat_off0 ^ (uint32_t)(op & 3)) << 4),
-                   tile + t * 1024);
+      const int g = FP8 ? 0 : op >> 2, j = op & 3;
+      const int t0 = FP8 ? 8 * w : 4 * w + 16 * g;      // first row of the group
+      constexpr int kStep = 1024 / kLatRow;              // rows per copy
+      if (ts.full) {
+        const char* const gb = ts.cp + (size_t)(ts.sb + t0) * kLatRow;
+        const lds_char* const lb = dst + t0 * kLatRow;
+        if (j == 0) dma_copy16_off<0>(gb, ln.cv[0], lb);
+        else if (j == 1) dma_copy16_off<1024>(gb, ln.cv[1], lb);
+        else if (j == 2) dma_copy16_off<2048>(gb, ln.cv[2], lb);
+        else dma_copy16_off<3072>(gb, ln.cv[3], lb);
       } else {
-        const int t = ln.tl8 + 8 * op;   // fsw(t) = fsw(tl8 + 8 (op & 1))
-        const int ts = min(sb + t, last);
-        dma_copy16(cp, (uint32_t)(ts * 512) + ((op & 1) ? ln.lat_off1 : ln.lat_off0),
-                   tile + 2 * (w + 4 * op) * 512);
+        const int t = t0 + kStep * j + (FP8 ? (ln.lane >> 5) : 0);
+        const int r = min(ts.sb + t, ts.last);
+        const uint32_t v = ((uint32_t)r << (FP8 ? 9 : 10)) + (ln.cv[j] & (FP8 ? 511u : ~0u));
+        dma_copy16_m0(ts.cp, v, dst + (t0 + kStep * j) * kLatRow);
       }
     } else if (op == kLatOps) {
-      const char* const rp = uniform_ptr(kr_base + idc * (kPage * kDr * 2));
-      dma_copy16(rp, (uint32_t)(min(sb + ln.rope_t, last) * 128) + ln.rope_off,
-                 tile + Gm::kRopeOff + w * 1024);
-    } else if constexpr (FP8) {
-      if (w == 0) {
-        const int ts = min(sb + (ln.lane & 31), last);
-        dma_copy4(uniform_ptr((const char*)p.ckv_scale + idc * (kPage * 4)), (uint32_t)(ts * 4),
-                  tile + Gm::kScaleOff);
+      if (ts.full) {
+        dma_copy16_m0(ts.rp + (size_t)(ts.sb + 8 * w) * 128, ln.rope_v, dst + Gm::kRopeOff + w * 1024);
+      } else {
+        const int t = 8 * w + (ln.lane >> 3);
+        dma_copy16_m0(ts.rp, ((uint32_t)min(ts.sb + t, ts.last) << 7) + (ln.rope_v & 127u),
+                      dst + Gm::kRopeOff + w * 1024);
       }
+    } else if constexpr (FP8) {
+      dma_copy4_m0(ts.sp, (uint32_t)min(ts.sb + (ln.lane & 31), ts.last) * 4, dst + Gm::kScaleOff);
     }
   };
-  constexpr int kMyCopies = (kCopies + 3) / 4;         // wave 0's count (the largest)
-  const int my_copies = (kCopies - w + 3) / 4;
+  // copies per wave and tile: bf16 8 latent + 1 rope; fp8 4 latent pairs
+  // + 1 rope + the scales
+  constexpr int kMyCopies = FP8 ? 6 : 9;
+  constexpr int kOpsPerTile = kMyCopies;
   // every step copies NT tiles: when the split's tile count is odd (64 rows),
   // the last step's second tile lies in the same page past the sequence end;
   // its slots repeat the last token and the mask gives them weight 0
-  auto issue_step = [&](const Lanes& ln, int s, int id) __attribute__((always_inline)) {
+  // the copies of step s into the buffers of step sdst
+  auto issue_step = [&](const Lanes& ln, int s, int sdst, int id) __attribute__((always_inline)) {
 #pragma clang loop unroll(full)
-    for (int t = 0; t < NT; ++t)
+    for (int t = 0; t < NT; ++t) {
+      const TileSrc ts = tile_src(s * NT + t, id, sdst * NT + t);
 #pragma clang loop unroll(full)
-      for (int op = 0; op < kMyCopies; ++op)
-        if (op < my_copies) copy_op(ln, s * NT + t, id, op);
+      for (int op = 0; op < kOpsPerTile; ++op) copy_op(ln, ts, op);
+    }
   };
   // page id of step s (both tiles of a 64-row step share one page)
   auto step_id = [&](int s) __attribute__((always_inline)) -> int {
     return __builtin_amdgcn_readfirstlane(ids[(s * NT * kTile) / kPage]);
   };
-  // this wave's copies of step s + 1 have landed: the copies of steps
-  // s + 2 .. s + LA that exist may still be in flight
-  auto wait_next = [&](int s) __attribute__((always_inline)) {
-    if constexpr (LA == 1) {
-      vm_wait<0>();
-    } else {
-      const int ahead = min(n_steps - 1, s + LA) - (s + 1);   // steps issued after s + 1
-      switch (ahead * NT * my_copies) {
-#define MLA_W(N) case N: vm_wait<N>(); break;
-        MLA_W(0) MLA_W(5) MLA_W(6) MLA_W(9) MLA_W(10) MLA_W(12) MLA_W(15) MLA_W(18)
-        MLA_W(20) MLA_W(24)
-#undef MLA_W
-        default: vm_wait<0>(); break;
-      }
-    }
-  };
-  static_assert((LA - 1) * NT * kMyCopies <= 32, "wait table");
+  static_assert((LA - 1) * NT * kMyCopies <= 63, "vmcnt range");
 
   if (__syncthreads_or(bad)) {
     write_uniform<ROWS>(p, b, k, row0, __builtin_nanf(""));
@@ -407,23 +421,31 @@ void decode_split_kernel(DecodeParams p) {
   // copy queue). LDS reads take immediate offsets from eight per-lane bases
   // per phase: a wave64 VALU instruction costs four cycles, so per-read
   // address arithmetic would cost more than the MFMAs it feeds.
-  auto step_body = [&](int s) __attribute__((always_inline)) {
+  auto step_body = [&](int s, auto first_c) __attribute__((always_inline)) {
+    constexpr bool kFirst = decltype(first_c)::value;
     const Lanes ln = lanes_now();
     const int t32 = ln.t32, h = ln.h;
     const int jt = s * NT + th;
     const int tl_off = (jt % NB) * kTileBytes;
     const lds_char* const tl = smem + tl_off;
     const int stok = tok0 + jt * kTile;
+    // Every step issues the copies of step s + LA; in the last LA steps,
+    // where no such step exists, they re-read the current page (an L2 hit)
+    // into the buffers of step s - 1, which nothing reads again. So every
+    // step has the same copy count and no copy needs a branch.
     const bool more = s + LA < n_steps;
-    const int cid = more ? step_id(s + LA) : 0;
-    // copy op o of the step's tile ct follows score MFMA 36 (ct + o / kMyCopies) / NT
+    const int sc = more ? s + LA : s;
+    const int cid = step_id(sc);
+    TileSrc cts[NT];
+#pragma clang loop unroll(full)
+    for (int ct = 0; ct < NT; ++ct) cts[ct] = tile_src(sc * NT + ct, cid, (s + LA) * NT + ct);
+    // copy slots: after MFMA f of the step (36 score MFMAs, then 32 of the
+    // aggregation), op o of the step's copies follows MFMA 68 o / kOps
     auto copy_slot = [&](int f) __attribute__((always_inline)) {
-      if (!more) return;
-      constexpr int kOps = NT * kMyCopies;
+      constexpr int kOps = NT * kOpsPerTile;
 #pragma clang loop unroll(full)
       for (int o = 0; o < kOps; ++o)
-        if (f == (36 * o) / kOps && (o % kMyCopies) < my_copies)
-          copy_op(ln, (s + LA) * NT + o / kMyCopies, cid, o % kMyCopies);
+        if (f == (68 * o) / kOps) copy_op(ln, cts[o / kOpsPerTile], o % kOpsPerTile);
     };
     // ---------------- scores S^T[token][row] --------------------------------
     // latent k-step ks reads chunk c = 2 ks + h (bf16) or 2 (ks / 2) + h (fp8,
@@ -442,7 +464,7 @@ void decode_split_kernel(DecodeParams p) {
         if (ks >= 32) return rope_frag(ks - 32);
         return lds_read_b128(smem + sbase[ks & 7] + 256 * (ks >> 3));
       };
-      constexpr int kRing = 8;
+      constexpr int kRing = 7;
       bf16x8_t ring[kRing];
 #pragma clang loop unroll(full)
       for (int f = 0; f < kRing; ++f) ring[f] = frag(f);
@@ -518,42 +540,54 @@ void decode_split_kernel(DecodeParams p) {
       for (int q = 0; q < 16; ++q)
         if (stok + 8 * (q >> 2) + 4 * h + (q & 3) >= lim) S0[q] = -INFINITY;
     }
-    float mx = S0[0];
+    // the row maximum over the tile (both lane halves), for the running true
+    // maximum -- and in the unit's first step, for the reference itself
+    auto tile_max = [&]() __attribute__((always_inline)) -> float {
+      float mx = fmaxf(fmaxf(S0[0], S0[1]), S0[2]);
 #pragma clang loop unroll(full)
-    for (int q = 1; q < 16; ++q) mx = fmaxf(mx, S0[q]);
-    {
+      for (int q = 3; q < 15; q += 2) mx = fmaxf(fmaxf(mx, S0[q]), S0[q + 1]);
+      mx = fmaxf(mx, S0[15]);
       const auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx = fmaxf(__uint_as_float(sw2[0]), __uint_as_float(sw2[1]));
+      return fmaxf(__uint_as_float(sw2[0]), __uint_as_float(sw2[1])) * sl;
+    };
+    if constexpr (kFirst) {
+      const float mt = tile_max();
+      m_true = fmaxf(m_true, mt);
+      if (m_r == -INFINITY) m_r = mt;   // first tile with a visible token (U = 0)
     }
-    const float mt = mx * sl;
-    m_true = fmaxf(m_true, mt);
-    if (m_r == -INFINITY) m_r = mt;   // first tile with a visible token (U = 0)
+    // After the unit's first step a row either has its reference or sees no
+    // token of this split at all (its later tiles only lie further right).
     const float nbase = (m_r == -INFINITY) ? 0.f : -m_r;
     // B operands of the aggregation's two k-steps: k-step kk holds the lane's
-    // values 8 kk..8 kk + 7, tokens 16 kk + {4h..4h+3, 8+4h..8+4h+3}
+    // values 8 kk..8 kk + 7, tokens 16 kk + {4h..4h+3, 8+4h..8+4h+3}; the row
+    // sum adds the same bf16 probabilities (fp8: before the token scale)
     bf16x8_t P[2];
     float ls = 0.f;
-    float e[16];
+    auto probs = [&](int kk) __attribute__((always_inline)) {
+      float tsc[16];   // fp8: the token scales of values 8 kk .. 8 kk + 7
+      if constexpr (FP8) {
 #pragma clang loop unroll(full)
-    for (int q = 0; q < 16; ++q) {
-      e[q] = fast_exp2(fmaf(S0[q], sl, nbase));
-      ls += e[q];
-    }
-    if constexpr (FP8) {
+        for (int j = 2 * kk; j < 2 * kk + 2; ++j) {
+          const f32x4_t sc = *(const MLA_LDS f32x4_t*)(tl + Gm::kScaleOff + (8 * j + 4 * h) * 4);
 #pragma clang loop unroll(full)
-      for (int j = 0; j < 4; ++j) {
-        const f32x4_t sc = *(const MLA_LDS f32x4_t*)(tl + Gm::kScaleOff + (8 * j + 4 * h) * 4);
-#pragma clang loop unroll(full)
-        for (int i = 0; i < 4; ++i) e[4 * j + i] *= sc[i];
+          for (int i = 0; i < 4; ++i) tsc[4 * j + i] = sc[i];
+        }
       }
-    }
+      uint32_t pk[4];
 #pragma clang loop unroll(full)
-    for (int kk = 0; kk < 2; ++kk)
-      P[kk] = __builtin_bit_cast(bf16x8_t, (u32x4_t){pack_bf16x2(e[8 * kk], e[8 * kk + 1]),
-                                                     pack_bf16x2(e[8 * kk + 2], e[8 * kk + 3]),
-                                                     pack_bf16x2(e[8 * kk + 4], e[8 * kk + 5]),
-                                                     pack_bf16x2(e[8 * kk + 6], e[8 * kk + 7])});
-    l_r += ls;
+      for (int q2 = 0; q2 < 4; ++q2) {
+        const int q = 8 * kk + 2 * q2;
+        const float e0 = fast_exp2(fmaf(S0[q], sl, nbase));
+        const float e1 = fast_exp2(fmaf(S0[q + 1], sl, nbase));
+        const uint32_t pl = pack_bf16x2(e0, e1);
+        ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pl),
+                                             (bf16x2_t){(__bf16)1.0f, (__bf16)1.0f}, ls, false);
+        pk[q2] = FP8 ? pack_bf16x2(e0 * tsc[q], e1 * tsc[q + 1]) : pl;
+      }
+      P[kk] = __builtin_bit_cast(bf16x8_t, (u32x4_t){pk[0], pk[1], pk[2], pk[3]});
+    };
+    probs(0);
+    if constexpr (kFirst) probs(1);
     // ---------------- aggregation U^T[dim][row] += C^T P^T -------------------
     // 32 A fragments (32 latent dims x 16 tokens, read transposed) through a
     // ring; the two k-steps of a dim block are 16 MFMAs apart.
@@ -581,7 +615,9 @@ void decode_split_kernel(DecodeParams p) {
 #pragma clang loop unroll(full)
       for (int b8 = 0; b8 < 8; ++b8) pbase[b8] = tl_off + tau * 512 + 16 * ((2 * b8 + G) ^ fs) + 8 * (i & 1);
     }
-    auto pfrag = [&](int e2) __attribute__((always_inline)) -> bf16x8_t {
+    // fp8 ring entries stay as raw codes until their MFMA (half the registers)
+    using RingT = std::conditional_t<FP8, i32x2_t, bf16x8_t>;
+    auto pfrag = [&](int e2) __attribute__((always_inline)) -> RingT {
       const int kk = e2 >> 4, db = e2 & 15;
       if constexpr (!FP8) {
         const int imm = 16 * kk * kLatRow + 256 * (db >> 2);
@@ -590,23 +626,32 @@ void decode_split_kernel(DecodeParams p) {
         return concat(lo, hi);
       } else {
         const int imm = 16 * kk * 512 + 256 * (db >> 3);
-        return fp8x8_to_bf16(
-            __builtin_amdgcn_ds_read_tr8_b64_v2i32((MLA_LDS i32x2_t*)(smem + pbase[db & 7] + imm)));
+        return __builtin_amdgcn_ds_read_tr8_b64_v2i32((MLA_LDS i32x2_t*)(smem + pbase[db & 7] + imm));
       }
     };
-    constexpr int kRingB = FP8 ? 12 : 7;
-    bf16x8_t ringb[kRingB];
+    constexpr int kRingB = FP8 ? 10 : 7;
+    RingT ringb[kRingB];
     __builtin_amdgcn_sched_barrier(0);
 #pragma clang loop unroll(full)
     for (int e2 = 0; e2 < kRingB; ++e2) ringb[e2] = pfrag(e2);
     __builtin_amdgcn_sched_barrier(0);
 #pragma clang loop unroll(full)
     for (int e2 = 0; e2 < 32; ++e2) {
-      const bf16x8_t av = ringb[e2 % kRingB];
+      bf16x8_t av;
+      if constexpr (FP8) av = fp8x8_to_bf16(ringb[e2 % kRingB]);
+      else av = ringb[e2 % kRingB];
       if (e2 + kRingB < 32) ringb[e2 % kRingB] = pfrag(e2 + kRingB);
       U[e2 & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, P[e2 >> 4], U[e2 & 15], 0, 0, 0);
+      if constexpr (!kFirst) {
+        // the second k-step's probabilities and the tile maximum run under
+        // the first k-step's MFMAs
+        if (e2 == 4) probs(1);
+        if (e2 == 9) m_true = fmaxf(m_true, tile_max());
+      }
+      copy_slot(36 + e2);
       __builtin_amdgcn_sched_barrier(0);
     }
+    l_r += ls;
   };
 
   for (int pass = 0; pass < 2; ++pass) {
@@ -617,18 +662,29 @@ void decode_split_kernel(DecodeParams p) {
     m_r = pass == 0 ? -INFINITY : m_true;
     l_r = 0.f;
     {
+      // steps 0 .. LA - 1; a step past the end re-reads step 0 (into a
+      // buffer nothing reads), so the loop's copy count stays uniform
       const Lanes ln = lanes_now();
-      issue_step(ln, 0, step_id(0));
+      issue_step(ln, 0, 0, step_id(0));
       vm_wait<0>();
-      for (int s = 1; s < LA && s < n_steps; ++s) issue_step(ln, s, step_id(s));
+      for (int s = 1; s < LA; ++s) {
+        const int ss = s < n_steps ? s : 0;
+        issue_step(ln, ss, s, step_id(ss));
+      }
     }
     lds_barrier();   // step 0 resident
-    for (int s = 0; s < n_steps; ++s) {
-      step_body(s);
-      // step s + 1 resident and step s's buffers free after the barrier
-      if (s + 1 < n_steps) wait_next(s);
+    // after each step: this wave's copies of step s + 1 have landed (those of
+    // the LA - 1 later steps may still fly); step s + 1 is resident and step
+    // s's buffers are free after the barrier
+    step_body(0, std::true_type{});
+    vm_wait<(LA - 1) * NT * kMyCopies>();
+    lds_barrier();
+    for (int s = 1; s < n_steps; ++s) {
+      step_body(s, std::false_type{});
+      vm_wait<(LA - 1) * NT * kMyCopies>();
       lds_barrier();
     }
+    vm_wait<0>();   // the tail's re-read copies land before LDS is reused
     // a second pass is needed when a row's maximum jumped past its reference
     // or a row sum left the finite range
     const bool jumped = m_true - m_r > kJump || !(l_r < INFINITY);

@@ -42,6 +42,53 @@ __device__ __forceinline__ void dma_copy4(const void* base, uint32_t voff, const
       : "memory");
 }
 
+// Four 1-KB copies sharing one LDS base: copy j moves lane i's 16 bytes from
+// base + vj + 1024 j to LDS byte lds + 1024 j + 16 i (the instruction offset
+// applies to the global and the LDS address alike). m0 is declared clobbered,
+// so the compiler keeps nothing of its own there across the copies.
+__device__ __forceinline__ void dma_copy16x4(const void* base, uint32_t v0, uint32_t v1, uint32_t v2,
+                                             uint32_t v3, const lds_char* lds) {
+  const uint32_t lds_addr = (uint32_t)(uintptr_t)lds;
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %5\n\t"
+      "global_load_lds_dwordx4 %2, %5 offset:1024\n\t"
+      "global_load_lds_dwordx4 %3, %5 offset:2048\n\t"
+      "global_load_lds_dwordx4 %4, %5 offset:3072"
+      :
+      : "s"(lds_addr), "v"(v0), "v"(v1), "v"(v2), "v"(v3), "s"(base)
+      : "memory", "m0");
+}
+
+// One 1-KB copy at instruction offset OFF (added to the global and the LDS
+// address alike) with m0 declared clobbered: several copies can share one
+// global base and one LDS base, with the per-copy offset in the instruction.
+template <int OFF>
+__device__ __forceinline__ void dma_copy16_off(const void* base, uint32_t voff, const lds_char* lds) {
+  const uint32_t lds_addr = (uint32_t)(uintptr_t)lds;
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 offset:%3"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(base), "i"(OFF)
+               : "memory", "m0");
+}
+
+// Single 16-byte and 4-byte copies with m0 declared clobbered (no restore).
+__device__ __forceinline__ void dma_copy16_m0(const void* base, uint32_t voff, const lds_char* lds) {
+  const uint32_t lds_addr = (uint32_t)(uintptr_t)lds;
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(base)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma_copy4_m0(const void* base, uint32_t voff, const lds_char* lds) {
+  const uint32_t lds_addr = (uint32_t)(uintptr_t)lds;
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(base)
+               : "memory", "m0");
+}
+
 // Wait until at most N of this wave's copies (and other vector memory loads)
 // are in flight; they complete in issue order.
 template <int N>
