@@ -1,0 +1,634 @@
+// Paged absorbed-MLA decode on gfx950 MFMA for bf16 caches, software
+// pipelined across tiles.
+//
+// A workgroup of four waves (one per SIMD) owns a work unit: sequence b,
+// split k and 128 query rows, 32 per wave. The split's cache streams through
+// LDS in tiles of 32 tokens (half a page): 512 latent and 64 rope elements
+// per token, the 576-element cache of PaperTrace "02 · DeepSeek-V2
+// analysis", section 1.3. Every wave reads every tile.
+//
+// Each wave is a complete attention worker for its 32 rows on the 32x32x16
+// bf16 MFMA: the absorbed queries stay in registers as the B operands of the
+// score S^T[token][row] = K[token][576] Q^T (section 1.3, eq. 18; the
+// 1/sqrt(192) scale is folded into the exponent), the online softmax of a
+// row runs in the lane that owns it, and the latent aggregate
+// U^T[dim][row] += C^T[dim][token] P^T[token][row] accumulates in the 256
+// accumulation registers, reading the tile transposed (ds_read_b64_tr_b16).
+// W^UV is applied afterwards (section 6.1).
+//
+// One wave per SIMD issues about one instruction per five cycles, so a step
+// that ran the score, then the softmax, then the aggregation would leave the
+// matrix unit idle through every phase boundary. Step s instead interleaves
+// the aggregation of tile s with the score MFMAs of tile s + 1 in one stream
+// of 68 MFMAs, and the softmax of tile s + 1 runs under the last aggregation
+// MFMAs; tile s + 3 is copied into the buffer freed by tile s - 1 in the
+// same step. Four tile buffers: s (aggregation), s + 1 (score), s + 2
+// (landed or landing) and s + 3 (being copied).
+//
+// Page copies are asynchronous (global_load_lds_dwordx4, 1 KB per
+// instruction), spread over the first part of the step, and every wave waits
+// for its own copies with vmcnt before the barrier that publishes them. A
+// copy never reads past the sequence: slots beyond its last token repeat the
+// last token, and the mask gives them weight exactly 0.
+//
+// The unit ends by writing either u = U / l and lse (one split), or partials
+// for the log-sum-exp combine: bf16 u = U / l with fp32 (m, l) when the
+// output is bf16, else fp32 (m, l, U).
+#include <type_traits>
+
+#include "dma.h"
+#include "mla_device.h"
+#include "mla_internal.h"
+
+namespace mla {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kTile = 32;
+constexpr int kRows = 128;                 // query rows per workgroup, 32 per wave
+constexpr int kNB = 4;                     // tile buffers
+constexpr int kLatRow = 1024;              // bytes of one token's latent
+constexpr int kRopeOff = kTile * kLatRow;  // rope rows of 128 B
+constexpr int kTileBytes = kRopeOff + kTile * 128;
+constexpr int kOffIds = kNB * kTileBytes;
+constexpr int kLdsBytes = kOffIds + kMaxSplitPages * 4;
+static_assert(kLdsBytes <= 163840, "LDS budget");
+constexpr int kCopies = 9;                 // copies per wave and tile
+constexpr int kSlots = 68;                 // MFMAs of a steady-state step
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// LDS swizzles, chosen so that every read pattern touches each of the 64
+// banks once per pass (16-B reads serve 16 lanes per pass: the 4-lane quads
+// of a half-wave split by the parity of the quad index; transposed reads
+// serve a half-wave per pass):
+//  * latent rows (1 KB): 16-B chunk c of token t at c ^ gsw(t),
+//    gsw(t) = ((t & 3) << 2) | ((t >> 2) & 3);
+//  * rope rows (128 B): 16-B chunk c of token t at c ^ ((t >> 1) & 7).
+__device__ __forceinline__ int gsw(int t) { return ((t & 3) << 2) | ((t >> 2) & 3); }
+__device__ __forceinline__ int swz_rope(int t) { return (t >> 1) & 7; }
+
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N <= 63, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Score MFMAs with VGPR accumulators (the 256 accumulation registers hold
+// U). The hardware does not interlock an MFMA result against VALU reads:
+// score_fence() pads the gap before the VALU reads the scores.
+__device__ __forceinline__ void mfma_sc0(f32x16_t& c, const bf16x8_t& a, const bf16x8_t& b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_sc(f32x16_t& c, const bf16x8_t& a, const bf16x8_t& b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void score_fence(f32x16_t& a, f32x16_t& b) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a), "+v"(b));
+}
+
+// Largest excess (log2 units) of a score over its row's reference maximum in
+// the first pass: probabilities stay below 2^32, row sums below 2^48.
+constexpr float kJump = 32.0f;
+
+// Slot schedule of a steady-state step (68 MFMAs): two aggregation MFMAs
+// whose operands are read before the step's barrier, then nine groups of
+// four score MFMAs (chains A B A B: an MFMA's chain partner issued two slots
+// earlier has finished) and one aggregation MFMA, then 21 aggregation MFMAs
+// under which the softmax of the scored tile runs, one stage every other slot.
+constexpr int kLeadG = 2;
+constexpr int kGroups = 9;
+constexpr int kTailFrom = kLeadG + 5 * kGroups;    // 47
+__host__ __device__ constexpr bool slot_is_score(int i) {
+  return i >= kLeadG && i < kTailFrom && (i - kLeadG) % 5 != 4;
+}
+// score k-step of a score slot / aggregation index of an aggregation slot
+__host__ __device__ constexpr int slot_index(int i) {
+  if (i < kLeadG) return i;
+  if (i < kTailFrom) {
+    const int t = (i - kLeadG) / 5, r = (i - kLeadG) % 5;
+    return r < 4 ? 4 * t + r : kLeadG + t;
+  }
+  return kLeadG + kGroups + (i - kTailFrom);
+}
+constexpr int kLastScore = kTailFrom - 2;          // slot of k-step 35
+// softmax stage at a tail slot (-1: none): stages 0-9 every other slot,
+// ending at the step's last slot
+__host__ __device__ constexpr int stage_at(int i) {
+  return (i >= kSlots - 19 && (kSlots - 1 - i) % 2 == 0) ? 9 - (kSlots - 1 - i) / 2 : -1;
+}
+// copy slots: op o of the step's nine copies follows MFMA 5 o + 4
+__host__ __device__ constexpr int copy_at(int i) {
+  return (i >= 4 && (i - 4) % 5 == 0 && (i - 4) / 5 < kCopies) ? (i - 4) / 5 : -1;
+}
+// the page id for the next step's copies is read from LDS after slot 30 and
+// moved to a scalar after slot 40
+constexpr int kIdRead = 30, kIdUse = 40;
+// aggregation index e2 = 15 (the last use of the first probability k-step)
+constexpr int kLastP0 = kTailFrom + 15 - (kLeadG + kGroups);
+
+// Every row of the unit gets (m, l, U) = (v, v, v): marks out-of-range
+// sequences and page ids with NaN.
+__device__ void write_uniform(const DecodeParams& p, int b, int k, int row0, float v) {
+  const int tid = threadIdx.x;
+  const int nrows = min(kRows, p.R - row0);
+  for (int e = tid; e < nrows * kDc; e += kThreads) {
+    const int r = row0 + e / kDc, d = e % kDc;
+    if (p.n_split == 1) {
+      const size_t o = ((size_t)b * p.R + r) * kDc + d;
+      if (p.out_bf16) ((uint16_t*)p.out)[o] = f2bf(v);
+      else ((float*)p.out)[o] = v;
+    } else {
+      const size_t o = (((size_t)b * p.n_split + k) * p.R + r) * kDc + d;
+      if (p.part_bf16) ((uint16_t*)p.part_u)[o] = f2bf(v);
+      else ((float*)p.part_u)[o] = v;
+    }
+  }
+  for (int r = row0 + tid; r < row0 + nrows; r += kThreads) {
+    if (p.n_split == 1) {
+      if (p.lse) p.lse[(size_t)b * p.R + r] = v;
+    } else {
+      float* ml = p.part_ml + (((size_t)b * p.n_split + k) * p.R + r) * 2;
+      ml[0] = v;
+      ml[1] = v;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void decode_pipe_kernel(DecodeParams p) {
+  __shared__ __attribute__((aligned(16))) char smem_raw[kLdsBytes];
+  lds_char* const smem = (lds_char*)smem_raw;
+
+  const int bid = blockIdx.x;
+  const int unit = (bid % kNumXcd) * p.per_xcd + bid / kNumXcd;
+  if (unit >= p.n_units) return;
+  const int g_unit = unit % p.G;
+  const int bk = unit / p.G;
+  const int k = bk % p.n_split;
+  const int b = bk / p.n_split;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  __builtin_assume(w >= 0 && w < kThreads / 64);
+
+  const int row0 = g_unit * kRows;
+  const int L = p.seq_lens[b];
+  const int tok0 = k * p.split_tokens;
+  const int tok1 = min(tok0 + p.split_tokens, L);
+  const int pg_begin = tok0 / kPage;
+  const int pg_end = (tok1 + kPage - 1) / kPage;
+  const int n_tiles = (tok1 - tok0 + kTile - 1) / kTile;
+  const bool seq_bad = (L < p.T) || (L > p.max_seq_len) ||
+                       ((L + kPage - 1) / kPage > p.max_pages) ||
+                       (pg_end - pg_begin) > kMaxSplitPages;
+  if (seq_bad) {
+    write_uniform(p, b, k, row0, __builtin_nanf(""));
+    return;
+  }
+  if (tok0 >= tok1) return;   // split past the end of the sequence: no partial
+
+  // ---- page ids of the split (global -> LDS), queries -> registers --------
+  int* const ids = (int*)(smem_raw + kOffIds);
+  const int32_t* const btrow = p.block_table + (size_t)b * p.max_pages;
+  const int n_pg = pg_end - pg_begin;
+  int idr[kMaxSplitPages / kThreads];
+#pragma clang loop unroll(full)
+  for (int i = 0; i < kMaxSplitPages / kThreads; ++i) {
+    const int j = tid + i * kThreads;
+    idr[i] = j < n_pg ? btrow[pg_begin + j] : 0;
+  }
+
+  // Absorbed queries of the wave's 32 rows as MFMA B fragments, lane = row
+  // (lane & 31), half h = lane >> 5: 32 latent k-steps (dims 16 ks + 8h..+7)
+  // and 4 rope k-steps of 16.
+  const int my_row = row0 + 32 * w + (lane & 31);
+  const int h = lane >> 5;
+  const int t32 = lane & 31;
+  bf16x8_t qB[36];
+  int lim;
+  {
+    const bool live = my_row < p.R;
+    const size_t qrow = (size_t)b * p.R + (live ? my_row : 0);
+    const uint16_t* ql = (const uint16_t*)p.q_lat + qrow * kDc + 8 * h;
+    const uint16_t* qr = (const uint16_t*)p.q_rope + qrow * kDr + 8 * h;
+#pragma clang loop unroll(full)
+    for (int ks = 0; ks < 36; ++ks) {
+      const bf16x8_t v = load_bf16x8(ks >= 32 ? qr + 16 * (ks - 32) : ql + 16 * ks);
+      qB[ks] = live ? v : (bf16x8_t){0, 0, 0, 0, 0, 0, 0, 0};
+    }
+    // visible-token limit of the row: s < min(L - T + t + 1, tok1)
+    const int t = live ? my_row / p.H : 0;
+    lim = min(L - p.T + t + 1, tok1);
+  }
+  // the group's earliest limit: tiles ending before it need no mask
+  const int lim_min = min(L - p.T + min(row0, p.R - 1) / p.H + 1, tok1);
+
+  bool bad = false;
+#pragma clang loop unroll(full)
+  for (int i = 0; i < kMaxSplitPages / kThreads; ++i) {
+    const int j = tid + i * kThreads;
+    if (j < n_pg) {
+      bad |= (idr[i] < 0) || (idr[i] >= p.n_pages);
+      ids[j] = idr[i];
+    }
+  }
+  if (__syncthreads_or(bad)) {
+    write_uniform(p, b, k, row0, __builtin_nanf(""));
+    return;
+  }
+  // (the barrier above also published the page ids)
+  const float sl = p.scale_log2;
+
+  // ---- per-lane LDS offsets within a tile buffer ---------------------------------
+  // Recomputed from a laundered lane index where needed (a few VALU
+  // instructions) instead of being kept live through the passes.
+  // score: latent k-step ks reads chunk 2 ks + h of token t32 at
+  //   sb8[ks & 7] + 256 (ks >> 3); rope k-step r reads rb4[r]
+  // aggregation: the 16-lane group G of half h reads dims 16 G + 4 (i & 3) of
+  // token rows 16 kk + 4h + i / 4 (lo) and 16 kk + 8 + 4h + i / 4 (hi); dim
+  // block db = 4 a + bb sits at 64 (bb ^ (i / 4)) + 256 a in the row
+  struct Offs {
+    int sb8[8], rb4[4], pb8[8];
+  };
+  auto offsets = [&]() __attribute__((always_inline)) -> Offs {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int t = ln & 31, hh = ln >> 5;
+    Offs o;
+#pragma clang loop unroll(full)
+    for (int j = 0; j < 8; ++j) o.sb8[j] = t * kLatRow + 16 * ((2 * j + hh) ^ gsw(t));
+#pragma clang loop unroll(full)
+    for (int r = 0; r < 4; ++r) o.rb4[r] = kRopeOff + t * 128 + 16 * ((2 * r + hh) ^ swz_rope(t));
+    const int i = ln & 15, G = (ln >> 4) & 1;
+    const int c_lo = 2 * G + ((i >> 1) & 1);
+    const int tr_row = (4 * hh + (i >> 2)) * kLatRow;
+#pragma clang loop unroll(full)
+    for (int bb = 0; bb < 4; ++bb) {
+      const int off = tr_row + 64 * (bb ^ (i >> 2)) + 8 * (i & 1);
+      o.pb8[bb] = off + 16 * (c_lo ^ hh);
+      o.pb8[4 + bb] = off + 8 * kLatRow + 16 * (c_lo ^ (hh + 2));
+    }
+    return o;
+  };
+  // copies: latent row 4w + 16g + j takes chunk lane ^ (4j + w) (its gsw);
+  // rope token 8w + lane / 8 takes chunk (lane & 7) ^ swz_rope(token)
+  const uint32_t lane16 = (uint32_t)lane << 4;
+  const uint32_t rope_v = (uint32_t)((lane >> 3) * 128 + (((lane & 7) ^ swz_rope(8 * w + (lane >> 3))) << 4));
+
+  // ---- page copies ------------------------------------------------------------
+  const char* const ckv_base = (const char*)p.ckv;
+  const char* const kr_base = (const char*)p.kr;
+  struct TileSrc {
+    const char* cp;
+    const char* rp;
+    int lds, sb, last;
+  };
+  // tile jt of the split into buffer jdst: a tile past the split's end
+  // re-reads the split's last tile
+  auto page_slot = [&](int jt) __attribute__((always_inline)) -> int {
+    return (min(jt, n_tiles - 1) * kTile) / kPage;
+  };
+  auto tile_src = [&](int jt, int jdst, int id) __attribute__((always_inline)) -> TileSrc {
+    const int jc = min(jt, n_tiles - 1);
+    const int t0 = tok0 + jc * kTile;                  // first token of the tile
+    const size_t idc = (size_t)id;                     // checked in [0, n_pages)
+    TileSrc ts;
+    ts.cp = ckv_base + idc * (kPage * kLatRow);
+    ts.rp = kr_base + idc * (kPage * kDr * 2);
+    ts.lds = (jdst % kNB) * kTileBytes;
+    ts.sb = t0 & (kPage - 1);
+    ts.last = min(L - 1 - (t0 - ts.sb), kPage - 1);    // in [0, 63]
+    return ts;
+  };
+  // copy op `op` (0-8) of a tile by this wave: ops 0-7 latent row
+  // 4w + 16 (op / 4) + op % 4, op 8 the rope of tokens 8w..8w + 7. The fast
+  // form assumes every slot of the tile holds a token (the copies of a row
+  // group share one base, the row's offset rides in the instruction); the
+  // safe form reads page slot min(sb + t, last) for slot sb + t.
+  auto copy_op = [&](const TileSrc& ts, int op, auto safe_c) __attribute__((always_inline)) {
+    constexpr bool kSafe = decltype(safe_c)::value;
+    const lds_char* const dst = smem + ts.lds;
+    if (op < 8) {
+      const int g = op >> 2, j = op & 3;
+      const int t0 = 4 * w + 16 * g;
+      const uint32_t cv = lane16 ^ (uint32_t)((4 * j + w) << 4);
+      if constexpr (!kSafe) {
+        const char* const gb = ts.cp + (size_t)(ts.sb + t0) * kLatRow;
+        const lds_char* const lb = dst + t0 * kLatRow;
+        if (j == 0) dma_copy16_off<0>(gb, cv, lb);
+        else if (j == 1) dma_copy16_off<1024>(gb, cv, lb);
+        else if (j == 2) dma_copy16_off<2048>(gb, cv, lb);
+        else dma_copy16_off<3072>(gb, cv, lb);
+      } else {
+        const int r = min(ts.sb + t0 + j, ts.last);
+        dma_copy16_m0(ts.cp + (size_t)r * kLatRow, cv, dst + (t0 + j) * kLatRow);
+      }
+    } else {
+      if constexpr (!kSafe) {
+        dma_copy16_m0(ts.rp + (size_t)(ts.sb + 8 * w) * 128, rope_v, dst + kRopeOff + w * 1024);
+      } else {
+        const int t = 8 * w + (lane >> 3);
+        dma_copy16_m0(ts.rp, ((uint32_t)min(ts.sb + t, ts.last) << 7) + (rope_v & 127u),
+                      dst + kRopeOff + w * 1024);
+      }
+    }
+  };
+  auto read_id = [&](int jt) __attribute__((always_inline)) -> int {
+    return __builtin_amdgcn_readfirstlane(ids[page_slot(jt)]);
+  };
+  auto copy_tile = [&](int jt, int jdst) __attribute__((always_inline)) {
+    const TileSrc ts = tile_src(jt, jdst, read_id(jt));
+#pragma clang loop unroll(full)
+    for (int op = 0; op < kCopies; ++op) copy_op(ts, op, std::true_type{});
+  };
+
+  // Each row's reference maximum is fixed in the first tile, where every row
+  // with a visible token in the split sees one (the split's first token is
+  // visible to every row that sees any), so the latent aggregate in the MFMA
+  // accumulators is never rescaled inside the loop. Should a later tile's
+  // maximum exceed the reference by more than kJump (log2 units) -- or a row
+  // sum overflow -- the unit runs a second pass over its tiles with every
+  // reference at the true row maximum found by the first.
+  f32x16_t U[16];                            // U^T: dims 32 db + 8 (q / 4) + 4h + q % 4
+  float m_r, l_r;                            // reference max (log2 units); lane's share of l
+  float m_true = -INFINITY;                  // running true row maximum (log2 units)
+
+  // ---- score pieces -----------------------------------------------------------
+  auto sfrag = [&](const Offs& o, int sbuf, int ks) __attribute__((always_inline)) -> bf16x8_t {
+    if (ks >= 32) return lds_read_b128(smem + sbuf + o.rb4[ks - 32]);
+    return lds_read_b128(smem + sbuf + o.sb8[ks & 7] + 256 * (ks >> 3));
+  };
+  auto gfrag = [&](const Offs& o, int gbuf, int e2) __attribute__((always_inline)) -> bf16x8_t {
+    const int kk = e2 >> 4, db = e2 & 15;
+    const int imm = 16 * kk * kLatRow + 256 * (db >> 2);
+    const bf16x4_t lo = lds_read_tr16(smem + gbuf + o.pb8[db & 3] + imm);
+    const bf16x4_t hi = lds_read_tr16(smem + gbuf + o.pb8[4 + (db & 3)] + imm);
+    return concat(lo, hi);
+  };
+  // scores of tile jt -> probabilities (B operands of its two aggregation
+  // k-steps: k-step kk holds the lane's values 8 kk..8 kk + 7, tokens
+  // 16 kk + {4h..4h+3, 8+4h..8+4h+3}); the row sum adds the same bf16
+  // values. In ten stages, so that a step can spread them over its last
+  // MFMAs: 0 mask and maximum, 1 references, 2-9 two probabilities each
+  // (stages 2-5 fill P0, stages 6-9 fill P1).
+  struct SoftmaxState {
+    float nbase, ls;
+    uint32_t pk[8];
+  };
+  auto softmax_stage = [&](int st, f32x16_t& S, int jt, bool first, SoftmaxState& ss, bf16x8_t& P0,
+                           bf16x8_t& P1) __attribute__((always_inline)) {
+    if (st == 0) {
+      const int stok = tok0 + jt * kTile;
+      if (stok + kTile > lim_min) {
+#pragma clang loop unroll(full)
+        for (int q = 0; q < 16; ++q)
+          if (stok + 8 * (q >> 2) + 4 * h + (q & 3) >= lim) S[q] = -INFINITY;
+      }
+      float mx = fmaxf(fmaxf(S[0], S[1]), S[2]);
+#pragma clang loop unroll(full)
+      for (int q = 3; q < 15; q += 2) mx = fmaxf(fmaxf(mx, S[q]), S[q + 1]);
+      ss.nbase = fmaxf(mx, S[15]);
+    } else if (st == 1) {
+      const float mx = ss.nbase;
+      const auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      const float mt = fmaxf(__uint_as_float(sw2[0]), __uint_as_float(sw2[1])) * sl;
+      m_true = fmaxf(m_true, mt);
+      if (first && m_r == -INFINITY) m_r = mt;        // the row's reference (U = 0)
+      ss.nbase = (m_r == -INFINITY) ? 0.f : -m_r;
+      ss.ls = 0.f;
+    } else {
+      const int q = 2 * (st - 2);
+      const float e0 = fast_exp2(fmaf(S[q], sl, ss.nbase));
+      const float e1 = fast_exp2(fmaf(S[q + 1], sl, ss.nbase));
+      ss.pk[q >> 1] = pack_bf16x2(e0, e1);
+      ss.ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, ss.pk[q >> 1]),
+                                              (bf16x2_t){(__bf16)1.0f, (__bf16)1.0f}, ss.ls, false);
+      if (st == 5) P0 = __builtin_bit_cast(bf16x8_t, (u32x4_t){ss.pk[0], ss.pk[1], ss.pk[2], ss.pk[3]});
+      if (st == 9) {
+        P1 = __builtin_bit_cast(bf16x8_t, (u32x4_t){ss.pk[4], ss.pk[5], ss.pk[6], ss.pk[7]});
+        l_r += ss.ls;
+      }
+    }
+  };
+
+  bf16x8_t P[2];                              // probabilities of the tile being aggregated
+  // operands of slot i are read after the MFMA of slot i - kDist; the reads
+  // of a step's first kDist slots lead it (those of its aggregation MFMAs
+  // before the barrier that precedes the step)
+  constexpr int kDist = 3;
+  static_assert(kLeadG < kDist && slot_is_score(kLeadG), "lead reads");
+  bf16x8_t ring[kDist];
+  int gb[8], sb[8], rb[4];                    // this step's LDS bases (aggregation, score)
+  auto set_bases = [&](int gbuf, int sbuf) __attribute__((always_inline)) {
+    const Offs o = offsets();
+#pragma clang loop unroll(full)
+    for (int j = 0; j < 8; ++j) gb[j] = gbuf + o.pb8[j];
+#pragma clang loop unroll(full)
+    for (int j = 0; j < 8; ++j) sb[j] = sbuf + o.sb8[j];
+#pragma clang loop unroll(full)
+    for (int r = 0; r < 4; ++r) rb[r] = sbuf + o.rb4[r];
+  };
+  auto sread = [&](int ks) __attribute__((always_inline)) -> bf16x8_t {
+    if (ks >= 32) return lds_read_b128(smem + rb[ks - 32]);
+    return lds_read_b128(smem + sb[ks & 7] + 256 * (ks >> 3));
+  };
+  auto gread = [&](int e2) __attribute__((always_inline)) -> bf16x8_t {
+    const int kk = e2 >> 4, db = e2 & 15;
+    const int imm = 16 * kk * kLatRow + 256 * (db >> 2);
+    const bf16x4_t lo = lds_read_tr16(smem + gb[db & 3] + imm);
+    const bf16x4_t hi = lds_read_tr16(smem + gb[4 + (db & 3)] + imm);
+    return concat(lo, hi);
+  };
+  auto fetch = [&](int i) __attribute__((always_inline)) {
+    ring[i % kDist] = slot_is_score(i) ? sread(slot_index(i)) : gread(slot_index(i));
+  };
+  auto lead_reads = [&]() __attribute__((always_inline)) {
+#pragma clang loop unroll(full)
+    for (int i = 0; i < kLeadG; ++i) fetch(i);
+  };
+
+  // the first tile of a pass: 36 score MFMAs on two chains, then the softmax
+  // that fixes the references; the copies of tile 2 ride along
+  auto first_step = [&]() __attribute__((always_inline)) {
+    const TileSrc cts = tile_src(2, 2, read_id(2));
+    const Offs o = offsets();
+    constexpr int kRing = 7;
+    bf16x8_t fr[kRing];
+#pragma clang loop unroll(full)
+    for (int f = 0; f < kRing; ++f) fr[f] = sfrag(o, 0, f);
+    f32x16_t SA, SB;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma clang loop unroll(full)
+    for (int ks = 0; ks < 36; ++ks) {
+      const bf16x8_t av = fr[ks % kRing];
+      f32x16_t& acc = (ks & 1) ? SB : SA;
+      if (ks < 2) mfma_sc0(acc, av, qB[ks]);
+      else mfma_sc(acc, av, qB[ks]);
+      if (ks + kRing < 36) fr[ks % kRing] = sfrag(o, 0, ks + kRing);
+      if (ks % 4 == 1 && ks / 4 < kCopies) copy_op(cts, ks / 4, std::true_type{});
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    score_fence(SA, SB);
+    SA += SB;
+    SoftmaxState ss;
+#pragma clang loop unroll(full)
+    for (int st = 0; st < 10; ++st) softmax_stage(st, SA, 0, true, ss, P[0], P[1]);
+  };
+
+  // steady-state step s: aggregation of tile s (bases gb, probabilities P)
+  // interleaved with the scores of tile s + 1 (bases sb, rb), whose softmax
+  // refills P; the copies of tile s + 3 (page id cid) go to buffer
+  // (s + 3) % 4. Returns the page id for the next step's copies.
+  auto step = [&](int s, int cid, auto safe_c) __attribute__((always_inline)) -> int {
+    const TileSrc cts = tile_src(s + 3, s + 3, cid);
+#pragma clang loop unroll(full)
+    for (int i = kLeadG; i < kDist; ++i) fetch(i);
+    f32x16_t SA, SB;
+    SoftmaxState ss;
+    bf16x8_t P1n;
+    int idv = 0, nid = 0;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma clang loop unroll(full)
+    for (int i = 0; i < kSlots; ++i) {
+      if (slot_is_score(i)) {
+        const int ks = slot_index(i);
+        f32x16_t& acc = (ks & 1) ? SB : SA;
+        if (ks < 2) mfma_sc0(acc, ring[i % kDist], qB[ks]);
+        else mfma_sc(acc, ring[i % kDist], qB[ks]);
+      } else {
+        const int e2 = slot_index(i);
+        U[e2 & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % kDist], P[e2 >> 4], U[e2 & 15], 0, 0, 0);
+      }
+      if (i + kDist < kSlots) fetch(i + kDist);
+      if (copy_at(i) >= 0) copy_op(cts, copy_at(i), safe_c);
+      if (i == kIdRead) idv = ids[page_slot(s + 4)];
+      if (i == kIdUse) nid = __builtin_amdgcn_readfirstlane(idv);
+      if (i == kLastScore + 1) score_fence(SA, SB);
+      if (i == kTailFrom) SA += SB;
+      if (stage_at(i) >= 0) {
+        static_assert(kSlots - 9 > kLastP0, "P0 is rewritten after its last use");
+        softmax_stage(stage_at(i), SA, s + 1, false, ss, P[0], P1n);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    P[1] = P1n;
+    // next step's buffers: one tile further, modulo the ring
+    const int d = ((s + 1) % kNB == 0) ? -(kNB - 1) * kTileBytes : kTileBytes;
+    const int d2 = ((s + 2) % kNB == 0) ? -(kNB - 1) * kTileBytes : kTileBytes;
+#pragma clang loop unroll(full)
+    for (int j = 0; j < 8; ++j) gb[j] += d;
+#pragma clang loop unroll(full)
+    for (int j = 0; j < 8; ++j) sb[j] += d2;
+#pragma clang loop unroll(full)
+    for (int r = 0; r < 4; ++r) rb[r] += d2;
+    return nid;
+  };
+  static_assert(stage_at(kSlots - 1) == 9, "softmax stages fill the tail");
+
+  // the last tile: its aggregation alone
+  auto last_step = [&](int s) __attribute__((always_inline)) {
+    const int gbuf = (s % kNB) * kTileBytes;
+    const Offs o = offsets();
+    constexpr int kRing = 7;
+    bf16x8_t fr[kRing];
+#pragma clang loop unroll(full)
+    for (int e2 = 0; e2 < kRing; ++e2) fr[e2] = gfrag(o, gbuf, e2);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma clang loop unroll(full)
+    for (int e2 = 0; e2 < 32; ++e2) {
+      const bf16x8_t av = fr[e2 % kRing];
+      if (e2 + kRing < 32) fr[e2 % kRing] = gfrag(o, gbuf, e2 + kRing);
+      U[e2 & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, P[e2 >> 4], U[e2 & 15], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma clang loop unroll(full)
+    for (int db = 0; db < 16; ++db)
+#pragma clang loop unroll(full)
+      for (int q = 0; q < 16; ++q) U[db][q] = 0.f;
+    m_r = pass == 0 ? -INFINITY : m_true;
+    l_r = 0.f;
+    // tiles 0 and 1 (a split of one tile re-reads it into buffer 1)
+    copy_tile(0, 0);
+    copy_tile(1, 1);
+    vm_wait<kCopies>();
+    lds_barrier();                                     // tile 0 resident
+    first_step();                                      // also copies tile 2
+    set_bases(0, kTileBytes);
+    int cid = read_id(3);
+    lead_reads();
+    vm_wait<kCopies>();
+    lds_barrier_keep<2 * kLeadG>();                    // tile 1 resident
+    // after step s: tile s + 2 resident (the copies of tile s + 3 may fly),
+    // tile s's buffer free; the lead reads of step s + 1 may still fly
+    const int n_fast = max(n_tiles - 4, 0);            // steps whose copy tile is full
+    for (int s = 0; s < n_fast; ++s) {
+      cid = step(s, cid, std::false_type{});
+      lead_reads();
+      vm_wait<kCopies>();
+      lds_barrier_keep<2 * kLeadG>();
+    }
+    for (int s = n_fast; s + 1 < n_tiles; ++s) {
+      cid = step(s, cid, std::true_type{});
+      lead_reads();
+      vm_wait<kCopies>();
+      lds_barrier_keep<2 * kLeadG>();
+    }
+    last_step(n_tiles - 1);
+    vm_wait<0>();   // the re-read copies land before LDS is reused
+    // a second pass is needed when a row's maximum jumped past its reference
+    // or a row sum left the finite range
+    const bool jumped = m_true - m_r > kJump || !(l_r < INFINITY);
+    if (!__syncthreads_or(jumped)) break;
+  }
+
+  // ---- finish -------------------------------------------------------------------
+  float l_row;
+  {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_r), __float_as_uint(l_r), false, false);
+    l_row = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  }
+  const bool direct = p.n_split == 1;
+  const size_t row_base = direct ? (size_t)b * p.R : ((size_t)b * p.n_split + k) * p.R;
+  const bool out16 = direct ? p.out_bf16 != 0 : p.part_bf16 != 0;
+  const bool normalise = direct || out16;   // fp32 partials keep U unnormalised
+  if (my_row < p.R) {
+    const float inv = normalise ? (l_row > 0.f ? 1.f / l_row : 0.f) : 1.f;
+    void* const dst = direct ? p.out : p.part_u;
+#pragma clang loop unroll(full)
+    for (int db = 0; db < 16; ++db) {
+#pragma clang loop unroll(full)
+      for (int j = 0; j < 4; ++j) {
+        const size_t o = (row_base + my_row) * kDc + 32 * db + 8 * j + 4 * h;
+        const f32x4_t v = (f32x4_t){U[db][4 * j], U[db][4 * j + 1], U[db][4 * j + 2], U[db][4 * j + 3]} * inv;
+        if (out16) {
+          *(u32x2_t*)((uint16_t*)dst + o) = (u32x2_t){pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        } else {
+          *(f32x4_t*)((float*)dst + o) = v;
+        }
+      }
+    }
+    if (lane < 32) {
+      if (direct) {
+        if (p.lse) p.lse[(size_t)b * p.R + my_row] = (m_r + log2f(l_row)) * kLn2;
+      } else {
+        p.part_ml[(row_base + my_row) * 2] = m_r;
+        p.part_ml[(row_base + my_row) * 2 + 1] = l_row;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode_pipe(const DecodeParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(decode_pipe_kernel, dim3(p.per_xcd * kNumXcd), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -105,4 +105,13 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// The same barrier letting the N most recent LDS reads of this wave stay in
+// flight (reads of data that no other wave overwrites before the next
+// barrier).
+template <int N>
+__device__ __forceinline__ void lds_barrier_keep() {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt field");
+  asm volatile("s_waitcnt lgkmcnt(%0)\n\ts_barrier" ::"i"(N) : "memory");
+}
+
 }  // namespace mla

@@ -69,7 +69,8 @@ Plan make_plan(const mla_decode_args* a) {
   // 128 rows per workgroup when the batch's row groups alone fill the GPU
   // (each page is then read by one workgroup); else 64, whose two row groups
   // of a sequence share every page through L2
-  if (a->ckv_dt != MLA_F32 && (int64_t)a->B * ((R + 127) / 128) >= kNumCu) pl.rows = 128;
+  if (a->ckv_dt == MLA_BF16 || (a->ckv_dt != MLA_F32 && (int64_t)a->B * ((R + 127) / 128) >= kNumCu))
+    pl.rows = 128;
   pl.G = (int)((R + pl.rows - 1) / pl.rows);
   if (a->split_tokens > 0) {
     pl.split_tokens = a->split_tokens;
@@ -287,7 +288,7 @@ int mla_decode_paged(const mla_decode_args* a, void* stream) {
   const hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if (a->ckv_dt == MLA_F32) e = launch_decode_simple_f32(p, s);
-  else if (a->ckv_dt == MLA_BF16) e = launch_decode_split(p, 0, pl.rows, s);
+  else if (a->ckv_dt == MLA_BF16) e = launch_decode_pipe(p, s);
   else e = launch_decode_split(p, 1, pl.rows, s);
   if (e != hipSuccess) return MLA_ERR_LAUNCH;
   if (pl.n_split > 1) {

@@ -53,11 +53,12 @@ def _args(mod, **kw):
 
 
 def test_plan_for_the_five_workloads(B):
-    # DeepSeek-V2 layer: 64 (sequence, 64-row group) pairs x 4 splits = 256 units
-    assert B.decode_plan(_args(B))[:2] == (1024, 4)
-    # 128K: 8 pairs x 32 splits
+    # DeepSeek-V2 layer (bf16 pool: 128-row groups): 32 (sequence, group)
+    # pairs x 8 splits = 256 units
+    assert B.decode_plan(_args(B))[:2] == (512, 8)
+    # 128K: 4 pairs x 64 splits
     assert B.decode_plan(_args(B, B=4, n_pages=8192, max_pages_per_seq=2048,
-                                   max_seq_len=131072))[:2] == (4096, 32)
+                                   max_seq_len=131072))[:2] == (2048, 64)
     # two-token fp8: 4 row groups x 128 sequences, no split
     st, ns, ws = B.decode_plan(_args(B, B=128, T=2, ckv_dt=B.MLA_FP8_E4M3, n_pages=16384,
                                      max_pages_per_seq=128, max_seq_len=8192))
