@@ -239,6 +239,21 @@ int mla_decode_plan(const mla_decode_args* args, int* split_tokens, int* n_split
 int mla_decode_paged(const mla_decode_args* args, void* stream);
 
 /*
+ * mla_decode_paged_noalloc -- mla_decode_paged for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). It ignores args->workspace and
+ * args->workspace_bytes and keeps the split partials in a static device
+ * array of MLA_NOALLOC_SCRATCH_BYTES per GPU instead, held until the process
+ * ends; nothing is allocated or freed. Calls whose partials would exceed it
+ * (mla_decode_plan's workspace_bytes) return MLA_ERR_WORKSPACE before any
+ * launch. Every call on one GPU shares that GPU's array: calls that overlap
+ * on one GPU (different streams, or host threads without ordering) race.
+ * Results are those of mla_decode_paged for the same arguments.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES (64u << 20)
+int mla_decode_paged_noalloc(const mla_decode_args* args, void* stream);
+
+/*
  * mla_out_proj -- each head's value up-projection applied after aggregation
  * (V2 analysis page, section 6.1: per-head aggregation first, then the head's
  * own matrix; the heads' matrices cannot be summed):

@@ -87,6 +87,8 @@ _lib.mla_decode_plan.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.POINTER(_i),
                                  ctypes.POINTER(_i), ctypes.POINTER(ctypes.c_size_t)]
 _lib.mla_decode_paged.restype = _i
 _lib.mla_decode_paged.argtypes = [ctypes.POINTER(DecodeArgs), _vp]
+_lib.mla_decode_paged_noalloc.restype = _i
+_lib.mla_decode_paged_noalloc.argtypes = [ctypes.POINTER(DecodeArgs), _vp]
 _lib.mla_rope_freq.restype = _i
 _lib.mla_rope_freq.argtypes = [_vp, _vp, _i, _vp, _i, _i, _i, _vp, _vp]
 _lib.mla_yarn_frequencies.restype = _i
@@ -107,7 +109,7 @@ _lib.mla_absorb_q_rope.argtypes = [_vp, _vp, _vp, _i, _i, _vp, _vp, _i, _vp, _i,
                                    _d, _vp, _vp]
 
 EXPORTED = ["mla_status_str", "mla_abi_version", "mla_absorb_q", "mla_rope",
-            "mla_decode_plan", "mla_decode_paged", "mla_out_proj", "mla_cache_append",
+            "mla_decode_plan", "mla_decode_paged", "mla_decode_paged_noalloc", "mla_out_proj", "mla_cache_append",
             "mla_rope_freq", "mla_yarn_frequencies", "mla_yarn_mscale", "mla_expand_kv",
             "mla_prefill_attn", "mla_absorb_q_rope"]
 
@@ -370,6 +372,21 @@ def decode_paged(q_lat: torch.Tensor, q_rope: torch.Tensor, cache: PagedCache, T
     _check("mla_decode_paged", _lib.mla_decode_paged(ctypes.byref(a), _stream(stream)))
     if w_uv is not None:
         return out, lse, o
+    return out, lse
+
+
+def decode_paged_noalloc(q_lat: torch.Tensor, q_rope: torch.Tensor, cache: PagedCache, T: int,
+                         softmax_scale: float, out: torch.Tensor, lse: Optional[torch.Tensor] = None,
+                         split_tokens: int = 0, stream=None):
+    """decode_paged through mla_decode_paged_noalloc: the split partials live in
+    the library's static per-device array, so the call allocates nothing
+    (out and lse are the caller's)."""
+    a = make_decode_args(q_lat, q_rope, cache, T, softmax_scale, out, lse, None, split_tokens)
+    a.q_lat, a.q_rope = _ptr(q_lat), _ptr(q_rope)
+    a.ckv, a.kr, a.ckv_scale = _ptr(cache.ckv), _ptr(cache.kr), _ptr(cache.ckv_scale)
+    a.block_table, a.seq_lens = _ptr(cache.block_table), _ptr(cache.seq_lens)
+    a.out, a.lse = _ptr(out), _ptr(lse)
+    _check("mla_decode_paged_noalloc", _lib.mla_decode_paged_noalloc(ctypes.byref(a), _stream(stream)))
     return out, lse
 
 

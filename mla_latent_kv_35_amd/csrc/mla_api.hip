@@ -3,6 +3,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "mla_extra.h"
 
@@ -101,6 +102,32 @@ Plan make_plan(const mla_decode_args* a) {
   return pl;
 }
 
+}  // namespace
+}  // namespace mla
+
+// Scratch of the allocation-free decode entry point: one array per device,
+// held until the process ends. Host code never uses the name itself (a
+// host-side stand-in); the device address comes from hipGetSymbolAddress,
+// once per device, with that device current.
+namespace mla {
+namespace {
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) char scratch[MLA_NOALLOC_SCRATCH_BYTES];
+void* g_scratch_ptr[kMaxDevices] = {};
+std::mutex g_scratch_mu;
+
+// The current device's scratch address, or nullptr when it cannot be had.
+void* scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
 }  // namespace
 }  // namespace mla
 
@@ -327,6 +354,20 @@ int mla_decode_paged(const mla_decode_args* a, void* stream) {
     if (e != hipSuccess) return MLA_ERR_LAUNCH;
   }
   return MLA_OK;
+}
+
+int mla_decode_paged_noalloc(const mla_decode_args* args, void* stream) {
+  if (!args) return MLA_ERR_NULL;
+  const int st = check_shape(args);
+  if (st != MLA_OK) return st;
+  const Plan pl = make_plan(args);
+  if (pl.n_split > 1 && pl.ws_bytes > (size_t)MLA_NOALLOC_SCRATCH_BYTES) return MLA_ERR_WORKSPACE;
+  void* const ws = scratch_ptr();
+  if (!ws) return MLA_ERR_LAUNCH;
+  mla_decode_args a = *args;
+  a.workspace = ws;
+  a.workspace_bytes = MLA_NOALLOC_SCRATCH_BYTES;
+  return mla_decode_paged(&a, stream);
 }
 
 int mla_out_proj(const void* u, const void* w_uv, void* o, int u_dt, int w_dt, int o_dt, int n_tok,
