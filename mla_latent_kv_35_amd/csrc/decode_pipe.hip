@@ -51,7 +51,10 @@ constexpr int kLatRow = 1024;              // bytes of one token's latent
 constexpr int kRopeOff = kTile * kLatRow;  // rope rows of 128 B
 constexpr int kTileBytes = kRopeOff + kTile * 128;
 constexpr int kOffIds = kNB * kTileBytes;
-constexpr int kLdsBytes = kOffIds + kMaxSplitPages * 4;
+// the first kQInLds query k-steps of every wave live in LDS, not registers
+constexpr int kQInLds = 2;
+constexpr int kOffQ = kOffIds + kMaxSplitPages * 4;
+constexpr int kLdsBytes = kOffQ + 4 * kQInLds * 1024;
 static_assert(kLdsBytes <= 163840, "LDS budget");
 constexpr int kCopies = 9;                 // copies per wave and tile
 constexpr int kSlots = 68;                 // MFMAs of a steady-state step
@@ -113,10 +116,16 @@ __host__ __device__ constexpr int slot_index(int i) {
   return kLeadG + kGroups + (i - kTailFrom);
 }
 constexpr int kLastScore = kTailFrom - 2;          // slot of k-step 35
-// softmax stage at a tail slot (-1: none): stages 0-9 every other slot,
-// ending at the step's last slot
-__host__ __device__ constexpr int stage_at(int i) {
-  return (i >= kSlots - 19 && (kSlots - 1 - i) % 2 == 0) ? 9 - (kSlots - 1 - i) / 2 : -1;
+// softmax stages of the scored tile: stages 0-5 (mask and maximum,
+// references, the first k-step's probabilities) at every third tail slot,
+// ending at the step's last slot; stages 6-9 (the second k-step's
+// probabilities, first used by aggregation index 16) in the next step's
+// score region
+__host__ __device__ constexpr int head_stage_at(int i) {
+  return (i >= kSlots - 16 && (kSlots - 1 - i) % 3 == 0) ? 5 - (kSlots - 1 - i) / 3 : -1;
+}
+__host__ __device__ constexpr int tail_stage_slot(int st) {
+  return st == 6 ? 0 : st == 7 ? 0 : st == 8 ? 1 : 1;
 }
 // copy slots: op o of the step's nine copies follows MFMA 5 o + 4
 __host__ __device__ constexpr int copy_at(int i) {
@@ -125,8 +134,14 @@ __host__ __device__ constexpr int copy_at(int i) {
 // the page id for the next step's copies is read from LDS after slot 30 and
 // moved to a scalar after slot 40
 constexpr int kIdRead = 30, kIdUse = 40;
-// aggregation index e2 = 15 (the last use of the first probability k-step)
+// slot of aggregation index 15 (the last use of the first probability
+// k-step) and of index 16 (the first use of the second)
 constexpr int kLastP0 = kTailFrom + 15 - (kLeadG + kGroups);
+constexpr int kFirstP1 = kTailFrom + 16 - (kLeadG + kGroups);
+static_assert(head_stage_at(kSlots - 1) == 5 && head_stage_at(kSlots - 16) == 0, "head stages");
+static_assert(kSlots - 16 > kTailFrom, "head stages follow the merged score");
+static_assert(kSlots - 1 > kLastP0, "P0 is rewritten after its last use");
+static_assert(tail_stage_slot(9) < kFirstP1, "P1 is complete before its first use");
 
 // Every row of the unit gets (m, l, U) = (v, v, v): marks out-of-range
 // sequences and page ids with NaN.
@@ -175,32 +190,21 @@ void decode_pipe_kernel(DecodeParams p) {
   __builtin_assume(w >= 0 && w < kThreads / 64);
 
   const int row0 = g_unit * kRows;
-  const int L = p.seq_lens[b];
   const int tok0 = k * p.split_tokens;
-  const int tok1 = min(tok0 + p.split_tokens, L);
   const int pg_begin = tok0 / kPage;
-  const int pg_end = (tok1 + kPage - 1) / kPage;
-  const int n_tiles = (tok1 - tok0 + kTile - 1) / kTile;
-  const bool seq_bad = (L < p.T) || (L > p.max_seq_len) ||
-                       ((L + kPage - 1) / kPage > p.max_pages) ||
-                       (pg_end - pg_begin) > kMaxSplitPages;
-  if (seq_bad) {
-    write_uniform(p, b, k, row0, __builtin_nanf(""));
-    return;
-  }
-  if (tok0 >= tok1) return;   // split past the end of the sequence: no partial
 
-  // ---- page ids of the split (global -> LDS), queries -> registers --------
-  int* const ids = (int*)(smem_raw + kOffIds);
+  // ---- one round trip: the sequence length, the split's page ids and the
+  // absorbed queries load together (none of the addresses depends on L) ----
+  const int L_raw = p.seq_lens[b];
   const int32_t* const btrow = p.block_table + (size_t)b * p.max_pages;
-  const int n_pg = pg_end - pg_begin;
+  const int pg_cap = min(p.split_tokens / kPage, p.max_pages - pg_begin);   // >= the split's pages
   int idr[kMaxSplitPages / kThreads];
 #pragma clang loop unroll(full)
   for (int i = 0; i < kMaxSplitPages / kThreads; ++i) {
     const int j = tid + i * kThreads;
-    idr[i] = j < n_pg ? btrow[pg_begin + j] : 0;
+    idr[i] = j < pg_cap ? btrow[pg_begin + j] : 0;
   }
-
+  const int id0_raw = btrow[pg_begin];
   // Absorbed queries of the wave's 32 rows as MFMA B fragments, lane = row
   // (lane & 31), half h = lane >> 5: 32 latent k-steps (dims 16 ks + 8h..+7)
   // and 4 rope k-steps of 16.
@@ -208,7 +212,6 @@ void decode_pipe_kernel(DecodeParams p) {
   const int h = lane >> 5;
   const int t32 = lane & 31;
   bf16x8_t qB[36];
-  int lim;
   {
     const bool live = my_row < p.R;
     const size_t qrow = (size_t)b * p.R + (live ? my_row : 0);
@@ -219,60 +222,28 @@ void decode_pipe_kernel(DecodeParams p) {
       const bf16x8_t v = load_bf16x8(ks >= 32 ? qr + 16 * (ks - 32) : ql + 16 * ks);
       qB[ks] = live ? v : (bf16x8_t){0, 0, 0, 0, 0, 0, 0, 0};
     }
-    // visible-token limit of the row: s < min(L - T + t + 1, tok1)
-    const int t = live ? my_row / p.H : 0;
-    lim = min(L - p.T + t + 1, tok1);
   }
-  // the group's earliest limit: tiles ending before it need no mask
-  const int lim_min = min(L - p.T + min(row0, p.R - 1) / p.H + 1, tok1);
 
-  bool bad = false;
-#pragma clang loop unroll(full)
-  for (int i = 0; i < kMaxSplitPages / kThreads; ++i) {
-    const int j = tid + i * kThreads;
-    if (j < n_pg) {
-      bad |= (idr[i] < 0) || (idr[i] >= p.n_pages);
-      ids[j] = idr[i];
-    }
-  }
-  if (__syncthreads_or(bad)) {
+  const int L = __builtin_amdgcn_readfirstlane(L_raw);
+  const int tok1 = min(tok0 + p.split_tokens, L);
+  const int pg_end = (tok1 + kPage - 1) / kPage;
+  const int n_tiles = (tok1 - tok0 + kTile - 1) / kTile;
+  const bool seq_bad = (L < p.T) || (L > p.max_seq_len) ||
+                       ((L + kPage - 1) / kPage > p.max_pages) ||
+                       (pg_end - pg_begin) > kMaxSplitPages;
+  if (seq_bad) {
+    vm_wait<0>();
     write_uniform(p, b, k, row0, __builtin_nanf(""));
     return;
   }
-  // (the barrier above also published the page ids)
-  const float sl = p.scale_log2;
+  if (tok0 >= tok1) {   // split past the end of the sequence: no partial
+    vm_wait<0>();
+    return;
+  }
+  // visible-token limit of the row: s < min(L - T + t + 1, tok1)
+  const int lim = min(L - p.T + (my_row < p.R ? my_row / p.H : 0) + 1, tok1);
 
-  // ---- per-lane LDS offsets within a tile buffer ---------------------------------
-  // Recomputed from a laundered lane index where needed (a few VALU
-  // instructions) instead of being kept live through the passes.
-  // score: latent k-step ks reads chunk 2 ks + h of token t32 at
-  //   sb8[ks & 7] + 256 (ks >> 3); rope k-step r reads rb4[r]
-  // aggregation: the 16-lane group G of half h reads dims 16 G + 4 (i & 3) of
-  // token rows 16 kk + 4h + i / 4 (lo) and 16 kk + 8 + 4h + i / 4 (hi); dim
-  // block db = 4 a + bb sits at 64 (bb ^ (i / 4)) + 256 a in the row
-  struct Offs {
-    int sb8[8], rb4[4], pb8[8];
-  };
-  auto offsets = [&]() __attribute__((always_inline)) -> Offs {
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    const int t = ln & 31, hh = ln >> 5;
-    Offs o;
-#pragma clang loop unroll(full)
-    for (int j = 0; j < 8; ++j) o.sb8[j] = t * kLatRow + 16 * ((2 * j + hh) ^ gsw(t));
-#pragma clang loop unroll(full)
-    for (int r = 0; r < 4; ++r) o.rb4[r] = kRopeOff + t * 128 + 16 * ((2 * r + hh) ^ swz_rope(t));
-    const int i = ln & 15, G = (ln >> 4) & 1;
-    const int c_lo = 2 * G + ((i >> 1) & 1);
-    const int tr_row = (4 * hh + (i >> 2)) * kLatRow;
-#pragma clang loop unroll(full)
-    for (int bb = 0; bb < 4; ++bb) {
-      const int off = tr_row + 64 * (bb ^ (i >> 2)) + 8 * (i & 1);
-      o.pb8[bb] = off + 16 * (c_lo ^ hh);
-      o.pb8[4 + bb] = off + 8 * kLatRow + 16 * (c_lo ^ (hh + 2));
-    }
-    return o;
-  };
+  int* const ids = (int*)(smem_raw + kOffIds);  // page ids of the split (filled below)
   // copies: latent row 4w + 16g + j takes chunk lane ^ (4j + w) (its gsw);
   // rope token 8w + lane / 8 takes chunk (lane & 7) ^ swz_rope(token)
   const uint32_t lane16 = (uint32_t)lane << 4;
@@ -345,6 +316,70 @@ void decode_pipe_kernel(DecodeParams p) {
     for (int op = 0; op < kCopies; ++op) copy_op(ts, op, std::true_type{});
   };
 
+  // ---- the first two tiles (both in the split's first page) go out now; a
+  // bad first page id is caught with the others below, before any tile is
+  // read --------------------------------------------------------------------
+  const int n_pg = pg_end - pg_begin;
+  const int id0 = __builtin_amdgcn_readfirstlane(id0_raw);
+  const bool id0_ok = id0 >= 0 && id0 < p.n_pages;
+  if (id0_ok) {
+    const TileSrc t0s = tile_src(0, 0, id0), t1s = tile_src(1, 1, id0);
+#pragma clang loop unroll(full)
+    for (int op = 0; op < kCopies; ++op) copy_op(t0s, op, std::true_type{});
+#pragma clang loop unroll(full)
+    for (int op = 0; op < kCopies; ++op) copy_op(t1s, op, std::true_type{});
+  }
+  // the group's earliest limit: tiles ending before it need no mask
+  const int lim_min = min(L - p.T + min(row0, p.R - 1) / p.H + 1, tok1);
+
+  bool bad = false;
+#pragma clang loop unroll(full)
+  for (int i = 0; i < kMaxSplitPages / kThreads; ++i) {
+    const int j = tid + i * kThreads;
+    if (j < n_pg) {
+      bad |= (idr[i] < 0) || (idr[i] >= p.n_pages);
+      ids[j] = idr[i];
+    }
+  }
+  if (__syncthreads_or(bad)) {
+    vm_wait<0>();                                    // the first copies land before LDS is released
+    write_uniform(p, b, k, row0, __builtin_nanf(""));
+    return;
+  }
+  // (the barrier above also published the page ids)
+  const float sl = p.scale_log2;
+
+  // ---- per-lane LDS offsets within a tile buffer ---------------------------------
+  // Recomputed from a laundered lane index where needed (a few VALU
+  // instructions) instead of being kept live through the passes.
+  // score: latent k-step ks reads chunk 2 ks + h of token t32 at
+  //   sb8[ks & 7] + 256 (ks >> 3); rope k-step r reads rb4[r]
+  // aggregation: the 16-lane group G of half h reads dims 16 G + 4 (i & 3) of
+  // token rows 16 kk + 4h + i / 4 (lo) and 16 kk + 8 + 4h + i / 4 (hi); dim
+  // block db = 4 a + bb sits at 64 (bb ^ (i / 4)) + 256 a in the row
+  struct Offs {
+    int sb8[8], rb4[4], pb8[8];
+  };
+  auto offsets = [&]() __attribute__((always_inline)) -> Offs {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int t = ln & 31, hh = ln >> 5;
+    Offs o;
+#pragma clang loop unroll(full)
+    for (int j = 0; j < 8; ++j) o.sb8[j] = t * kLatRow + 16 * ((2 * j + hh) ^ gsw(t));
+#pragma clang loop unroll(full)
+    for (int r = 0; r < 4; ++r) o.rb4[r] = kRopeOff + t * 128 + 16 * ((2 * r + hh) ^ swz_rope(t));
+    const int i = ln & 15, G = (ln >> 4) & 1;
+    const int c_lo = 2 * G + ((i >> 1) & 1);
+    const int tr_row = (4 * hh + (i >> 2)) * kLatRow;
+#pragma clang loop unroll(full)
+    for (int bb = 0; bb < 4; ++bb) {
+      const int off = tr_row + 64 * (bb ^ (i >> 2)) + 8 * (i & 1);
+      o.pb8[bb] = off + 16 * (c_lo ^ hh);
+      o.pb8[4 + bb] = off + 8 * kLatRow + 16 * (c_lo ^ (hh + 2));
+    }
+    return o;
+  };
   // Each row's reference maximum is fixed in the first tile, where every row
   // with a visible token in the split sees one (the split's first token is
   // visible to every row that sees any), so the latent aggregate in the MFMA
@@ -355,6 +390,12 @@ void decode_pipe_kernel(DecodeParams p) {
   f32x16_t U[16];                            // U^T: dims 32 db + 8 (q / 4) + 4h + q % 4
   float m_r, l_r;                            // reference max (log2 units); lane's share of l
   float m_true = -INFINITY;                  // running true row maximum (log2 units)
+
+  // the query operand of score k-step ks (the first kQInLds from LDS)
+  auto qop = [&](int ks) __attribute__((always_inline)) -> bf16x8_t {
+    if (ks < kQInLds) return lds_read_b128(smem + kOffQ + (w * kQInLds + ks) * 1024 + lane * 16);
+    return qB[ks];
+  };
 
   // ---- score pieces -----------------------------------------------------------
   auto sfrag = [&](const Offs& o, int sbuf, int ks) __attribute__((always_inline)) -> bf16x8_t {
@@ -371,15 +412,23 @@ void decode_pipe_kernel(DecodeParams p) {
   // scores of tile jt -> probabilities (B operands of its two aggregation
   // k-steps: k-step kk holds the lane's values 8 kk..8 kk + 7, tokens
   // 16 kk + {4h..4h+3, 8+4h..8+4h+3}); the row sum adds the same bf16
-  // values. In ten stages, so that a step can spread them over its last
-  // MFMAs: 0 mask and maximum, 1 references, 2-9 two probabilities each
-  // (stages 2-5 fill P0, stages 6-9 fill P1).
-  struct SoftmaxState {
+  // values. In ten stages, so that steps can spread them between MFMAs:
+  // 0 mask and maximum, 1 references, 2-5 the first k-step (P0), 6-9 the
+  // second (P1) from the scores' upper half kept in Sh.
+  struct SoftmaxCarry {
     float nbase, ls;
-    uint32_t pk[8];
+    float Sh[8];
+    uint32_t pk[4];
   };
-  auto softmax_stage = [&](int st, f32x16_t& S, int jt, bool first, SoftmaxState& ss, bf16x8_t& P0,
-                           bf16x8_t& P1) __attribute__((always_inline)) {
+  auto prob_pair = [&](float s0, float s1, SoftmaxCarry& c, uint32_t& pk) __attribute__((always_inline)) {
+    const float e0 = fast_exp2(fmaf(s0, sl, c.nbase));
+    const float e1 = fast_exp2(fmaf(s1, sl, c.nbase));
+    pk = pack_bf16x2(e0, e1);
+    c.ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk),
+                                           (bf16x2_t){(__bf16)1.0f, (__bf16)1.0f}, c.ls, false);
+  };
+  auto head_stage = [&](int st, f32x16_t& S, int jt, bool first, SoftmaxCarry& c, bf16x8_t& P0)
+      __attribute__((always_inline)) {
     if (st == 0) {
       const int stok = tok0 + jt * kTile;
       if (stok + kTile > lim_min) {
@@ -390,31 +439,36 @@ void decode_pipe_kernel(DecodeParams p) {
       float mx = fmaxf(fmaxf(S[0], S[1]), S[2]);
 #pragma clang loop unroll(full)
       for (int q = 3; q < 15; q += 2) mx = fmaxf(fmaxf(mx, S[q]), S[q + 1]);
-      ss.nbase = fmaxf(mx, S[15]);
+      c.nbase = fmaxf(mx, S[15]);
     } else if (st == 1) {
-      const float mx = ss.nbase;
+      const float mx = c.nbase;
       const auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
       const float mt = fmaxf(__uint_as_float(sw2[0]), __uint_as_float(sw2[1])) * sl;
       m_true = fmaxf(m_true, mt);
       if (first && m_r == -INFINITY) m_r = mt;        // the row's reference (U = 0)
-      ss.nbase = (m_r == -INFINITY) ? 0.f : -m_r;
-      ss.ls = 0.f;
+      c.nbase = (m_r == -INFINITY) ? 0.f : -m_r;
+      c.ls = 0.f;
     } else {
       const int q = 2 * (st - 2);
-      const float e0 = fast_exp2(fmaf(S[q], sl, ss.nbase));
-      const float e1 = fast_exp2(fmaf(S[q + 1], sl, ss.nbase));
-      ss.pk[q >> 1] = pack_bf16x2(e0, e1);
-      ss.ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, ss.pk[q >> 1]),
-                                              (bf16x2_t){(__bf16)1.0f, (__bf16)1.0f}, ss.ls, false);
-      if (st == 5) P0 = __builtin_bit_cast(bf16x8_t, (u32x4_t){ss.pk[0], ss.pk[1], ss.pk[2], ss.pk[3]});
-      if (st == 9) {
-        P1 = __builtin_bit_cast(bf16x8_t, (u32x4_t){ss.pk[4], ss.pk[5], ss.pk[6], ss.pk[7]});
-        l_r += ss.ls;
+      prob_pair(S[q], S[q + 1], c, c.pk[q >> 1]);
+      if (st == 5) {
+        P0 = __builtin_bit_cast(bf16x8_t, (u32x4_t){c.pk[0], c.pk[1], c.pk[2], c.pk[3]});
+#pragma clang loop unroll(full)
+        for (int j = 0; j < 8; ++j) c.Sh[j] = S[8 + j];
       }
+    }
+  };
+  auto tail_stage = [&](int st, SoftmaxCarry& c, bf16x8_t& P1) __attribute__((always_inline)) {
+    const int j = 2 * (st - 6);
+    prob_pair(c.Sh[j], c.Sh[j + 1], c, c.pk[j >> 1]);
+    if (st == 9) {
+      P1 = __builtin_bit_cast(bf16x8_t, (u32x4_t){c.pk[0], c.pk[1], c.pk[2], c.pk[3]});
+      l_r += c.ls;
     }
   };
 
   bf16x8_t P[2];                              // probabilities of the tile being aggregated
+  SoftmaxCarry carry;                         // the second half of P still to compute
   // operands of slot i are read after the MFMA of slot i - kDist; the reads
   // of a step's first kDist slots lead it (those of its aggregation MFMAs
   // before the barrier that precedes the step)
@@ -455,6 +509,9 @@ void decode_pipe_kernel(DecodeParams p) {
   auto first_step = [&]() __attribute__((always_inline)) {
     const TileSrc cts = tile_src(2, 2, read_id(2));
     const Offs o = offsets();
+    bf16x8_t qL[kQInLds];
+#pragma clang loop unroll(full)
+    for (int j = 0; j < kQInLds; ++j) qL[j] = qop(j);
     constexpr int kRing = 7;
     bf16x8_t fr[kRing];
 #pragma clang loop unroll(full)
@@ -465,17 +522,17 @@ void decode_pipe_kernel(DecodeParams p) {
     for (int ks = 0; ks < 36; ++ks) {
       const bf16x8_t av = fr[ks % kRing];
       f32x16_t& acc = (ks & 1) ? SB : SA;
-      if (ks < 2) mfma_sc0(acc, av, qB[ks]);
-      else mfma_sc(acc, av, qB[ks]);
+      const bf16x8_t qv = ks < kQInLds ? qL[ks] : qB[ks];
+      if (ks < 2) mfma_sc0(acc, av, qv);
+      else mfma_sc(acc, av, qv);
       if (ks + kRing < 36) fr[ks % kRing] = sfrag(o, 0, ks + kRing);
       if (ks % 4 == 1 && ks / 4 < kCopies) copy_op(cts, ks / 4, std::true_type{});
       __builtin_amdgcn_sched_barrier(0);
     }
     score_fence(SA, SB);
     SA += SB;
-    SoftmaxState ss;
 #pragma clang loop unroll(full)
-    for (int st = 0; st < 10; ++st) softmax_stage(st, SA, 0, true, ss, P[0], P[1]);
+    for (int st = 0; st < 6; ++st) head_stage(st, SA, 0, true, carry, P[0]);
   };
 
   // steady-state step s: aggregation of tile s (bases gb, probabilities P)
@@ -484,11 +541,12 @@ void decode_pipe_kernel(DecodeParams p) {
   // (s + 3) % 4. Returns the page id for the next step's copies.
   auto step = [&](int s, int cid, auto safe_c) __attribute__((always_inline)) -> int {
     const TileSrc cts = tile_src(s + 3, s + 3, cid);
+    bf16x8_t qL[kQInLds];
+#pragma clang loop unroll(full)
+    for (int j = 0; j < kQInLds; ++j) qL[j] = qop(j);
 #pragma clang loop unroll(full)
     for (int i = kLeadG; i < kDist; ++i) fetch(i);
     f32x16_t SA, SB;
-    SoftmaxState ss;
-    bf16x8_t P1n;
     int idv = 0, nid = 0;
     __builtin_amdgcn_sched_barrier(0);
 #pragma clang loop unroll(full)
@@ -496,8 +554,9 @@ void decode_pipe_kernel(DecodeParams p) {
       if (slot_is_score(i)) {
         const int ks = slot_index(i);
         f32x16_t& acc = (ks & 1) ? SB : SA;
-        if (ks < 2) mfma_sc0(acc, ring[i % kDist], qB[ks]);
-        else mfma_sc(acc, ring[i % kDist], qB[ks]);
+        const bf16x8_t qv = ks < kQInLds ? qL[ks] : qB[ks];
+        if (ks < 2) mfma_sc0(acc, ring[i % kDist], qv);
+        else mfma_sc(acc, ring[i % kDist], qv);
       } else {
         const int e2 = slot_index(i);
         U[e2 & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % kDist], P[e2 >> 4], U[e2 & 15], 0, 0, 0);
@@ -508,13 +567,12 @@ void decode_pipe_kernel(DecodeParams p) {
       if (i == kIdUse) nid = __builtin_amdgcn_readfirstlane(idv);
       if (i == kLastScore + 1) score_fence(SA, SB);
       if (i == kTailFrom) SA += SB;
-      if (stage_at(i) >= 0) {
-        static_assert(kSlots - 9 > kLastP0, "P0 is rewritten after its last use");
-        softmax_stage(stage_at(i), SA, s + 1, false, ss, P[0], P1n);
-      }
+#pragma clang loop unroll(full)
+      for (int st = 6; st < 10; ++st)
+        if (tail_stage_slot(st) == i) tail_stage(st, carry, P[1]);
+      if (head_stage_at(i) >= 0) head_stage(head_stage_at(i), SA, s + 1, false, carry, P[0]);
       __builtin_amdgcn_sched_barrier(0);
     }
-    P[1] = P1n;
     // next step's buffers: one tile further, modulo the ring
     const int d = ((s + 1) % kNB == 0) ? -(kNB - 1) * kTileBytes : kTileBytes;
     const int d2 = ((s + 2) % kNB == 0) ? -(kNB - 1) * kTileBytes : kTileBytes;
@@ -526,7 +584,6 @@ void decode_pipe_kernel(DecodeParams p) {
     for (int r = 0; r < 4; ++r) rb[r] += d2;
     return nid;
   };
-  static_assert(stage_at(kSlots - 1) == 9, "softmax stages fill the tail");
 
   // the last tile: its aggregation alone
   auto last_step = [&](int s) __attribute__((always_inline)) {
@@ -536,6 +593,8 @@ void decode_pipe_kernel(DecodeParams p) {
     bf16x8_t fr[kRing];
 #pragma clang loop unroll(full)
     for (int e2 = 0; e2 < kRing; ++e2) fr[e2] = gfrag(o, gbuf, e2);
+#pragma clang loop unroll(full)
+    for (int st = 6; st < 10; ++st) tail_stage(st, carry, P[1]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma clang loop unroll(full)
     for (int e2 = 0; e2 < 32; ++e2) {
@@ -553,10 +612,20 @@ void decode_pipe_kernel(DecodeParams p) {
       for (int q = 0; q < 16; ++q) U[db][q] = 0.f;
     m_r = pass == 0 ? -INFINITY : m_true;
     l_r = 0.f;
-    // tiles 0 and 1 (a split of one tile re-reads it into buffer 1)
-    copy_tile(0, 0);
-    copy_tile(1, 1);
+    // tiles 0 and 1 (a split of one tile re-reads it into buffer 1); the
+    // first pass's went out before the queries loaded
+    if (pass > 0) {
+      copy_tile(0, 0);
+      copy_tile(1, 1);
+    }
     vm_wait<kCopies>();
+    if (pass == 0) {
+      // (after the wait: an earlier store would wait for the first copies
+      // before the queries were needed)
+#pragma clang loop unroll(full)
+      for (int ks = 0; ks < kQInLds; ++ks)
+        *(MLA_LDS bf16x8_t*)(smem + kOffQ + (w * kQInLds + ks) * 1024 + lane * 16) = qB[ks];
+    }
     lds_barrier();                                     // tile 0 resident
     first_step();                                      // also copies tile 2
     set_bases(0, kTileBytes);
@@ -597,29 +666,50 @@ void decode_pipe_kernel(DecodeParams p) {
   const size_t row_base = direct ? (size_t)b * p.R : ((size_t)b * p.n_split + k) * p.R;
   const bool out16 = direct ? p.out_bf16 != 0 : p.part_bf16 != 0;
   const bool normalise = direct || out16;   // fp32 partials keep U unnormalised
-  if (my_row < p.R) {
-    const float inv = normalise ? (l_row > 0.f ? 1.f / l_row : 0.f) : 1.f;
-    void* const dst = direct ? p.out : p.part_u;
+  const float inv = normalise ? (l_row > 0.f ? 1.f / l_row : 0.f) : 1.f;
+  void* const dst = direct ? p.out : p.part_u;
+  if (out16) {
+    // bf16 rows through LDS (every wave's reads of the tiles ended at the
+    // pass loop's last barrier): the wave writes its 32 rows of 1 KB with
+    // 16-byte chunk c of row r at c ^ r, then stores one whole row per
+    // instruction
+    lds_char* const rows = smem + w * 32 * 1024;
+#pragma clang loop unroll(full)
+    for (int db = 0; db < 16; ++db) {
+#pragma clang loop unroll(full)
+      for (int j = 0; j < 4; ++j) {
+        const f32x4_t v = (f32x4_t){U[db][4 * j], U[db][4 * j + 1], U[db][4 * j + 2], U[db][4 * j + 3]} * inv;
+        const int c = 4 * db + j;                        // dims 32 db + 8 j .. + 7
+        *(MLA_LDS u32x2_t*)(rows + t32 * 1024 + ((c ^ t32) << 4) + 8 * h) =
+            (u32x2_t){pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      }
+    }
+    uint16_t* const out_rows = (uint16_t*)dst + (row_base + row0 + 32 * w) * kDc;
+    const int live_rows = min(32, p.R - (row0 + 32 * w));
+#pragma clang loop unroll(full)
+    for (int r = 0; r < 32; ++r) {
+      if (r < live_rows) {
+        const u32x4_t v = *(const MLA_LDS u32x4_t*)(rows + r * 1024 + ((lane ^ r) << 4));
+        *(u32x4_t*)(out_rows + r * kDc + lane * 8) = v;
+      }
+    }
+  } else if (my_row < p.R) {
 #pragma clang loop unroll(full)
     for (int db = 0; db < 16; ++db) {
 #pragma clang loop unroll(full)
       for (int j = 0; j < 4; ++j) {
         const size_t o = (row_base + my_row) * kDc + 32 * db + 8 * j + 4 * h;
         const f32x4_t v = (f32x4_t){U[db][4 * j], U[db][4 * j + 1], U[db][4 * j + 2], U[db][4 * j + 3]} * inv;
-        if (out16) {
-          *(u32x2_t*)((uint16_t*)dst + o) = (u32x2_t){pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-        } else {
-          *(f32x4_t*)((float*)dst + o) = v;
-        }
+        *(f32x4_t*)((float*)dst + o) = v;
       }
     }
-    if (lane < 32) {
-      if (direct) {
-        if (p.lse) p.lse[(size_t)b * p.R + my_row] = (m_r + log2f(l_row)) * kLn2;
-      } else {
-        p.part_ml[(row_base + my_row) * 2] = m_r;
-        p.part_ml[(row_base + my_row) * 2 + 1] = l_row;
-      }
+  }
+  if (my_row < p.R && lane < 32) {
+    if (direct) {
+      if (p.lse) p.lse[(size_t)b * p.R + my_row] = (m_r + log2f(l_row)) * kLn2;
+    } else {
+      p.part_ml[(row_base + my_row) * 2] = m_r;
+      p.part_ml[(row_base + my_row) * 2 + 1] = l_row;
     }
   }
 }
