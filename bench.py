@@ -29,7 +29,7 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0       # dense bf16 MFMA
 METRIC = "MLA decode tokens/s + achieved HBM GB/s (% of peak), B=32 H=128 S=4096 bf16"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic_dsv2_layer.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic_{}.json")
 
 
 def parse():
@@ -60,17 +60,19 @@ def copy_probe(mib: int) -> None:
 
 def kernel_source_digest() -> str:
     h = hashlib.sha256()
-    for f in ("decode_mfma.hip", "combine.hip", "dma.h", "mla_device.h", "mla_internal.h"):
+    for f in ("decode_pipe.hip", "decode_mfma.hip", "combine.hip", "dma.h", "mla_device.h",
+              "mla_internal.h"):
         with open(os.path.join(ROOT, "mla_latent_kv_35_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(launch_bytes: float):
-    """HBM bytes per decode launch from the committed rocprofv3 counter runs,
-    valid only while the kernel sources are the ones they were taken on."""
+def load_traffic(workload: str):
+    """HBM bytes per decode launch of this workload from the committed
+    rocprofv3 counter runs, valid only while the kernel sources are the ones
+    they were taken on."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(TRAFFIC_FILE.format(workload)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -271,13 +273,28 @@ def main():
     torch.cuda.synchronize()
     copy_gbps = 2 * n_cp * 5 / (c0e.elapsed_time(c1e) * 1e-3) / 1e9
     del cp_src, cp_dst
+    # and what a plain streaming read reaches (mla_stream_read over 2 GiB: the
+    # bound the decode's cache reads are held against)
+    n_rp = 2 << 30
+    rp_src = torch.ones(n_rp, dtype=torch.uint8, device="cuda")
+    rp_sink = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    mla.stream_read(rp_src, rp_sink)
+    r0e, r1e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    r0e.record(stream)
+    for _ in range(5):
+        mla.stream_read(rp_src, rp_sink)
+    r1e.record(stream)
+    torch.cuda.synchronize()
+    read_gbps = n_rp * 5 / (r0e.elapsed_time(r1e) * 1e-3) / 1e9
+    del rp_src, rp_sink
 
     tokens = cfg.B * cfg.T
     value = tokens * steps / el
     dec_s = dur_ms["decode"] * 1e-3
     achieved = cache_bytes / dec_s / 1e9
     flops = inp.total_tokens * cfg.H * cfg.T * O.decode_flops_per_row_token()
-    traffic = load_traffic(cache_bytes)
+    traffic = load_traffic(cfg.name)
     out = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -303,9 +320,13 @@ def main():
         "copy_context": {"what": "torch device-to-device copy of 1 GiB, read + write bytes / time",
                          "gbps": round(copy_gbps, 1),
                          "decode_hbm_over_copy": round(achieved / copy_gbps, 4)},
+        "read_probe": {"what": "mla_stream_read of 2 GiB (16-byte loads, read only)",
+                       "gbps": round(read_gbps, 1),
+                       "decode_hbm_over_read": round(achieved / read_gbps, 4)},
         "launch": "hip graph of %d steps per replay" % per_graph,
         "roofline": {
-            "kernel": "mla_decode_paged (split-KV kernel + log-sum-exp combine)",
+            "kernel": ("mla_decode_paged: split-KV kernel (decode_pipe_kernel for bf16 pools, "
+                       "decode_mfma_kernel for fp8) + log-sum-exp combine, timed together"),
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": PEAK_HBM_GBPS,

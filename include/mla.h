@@ -254,6 +254,18 @@ int mla_decode_paged(const mla_decode_args* args, void* stream);
 int mla_decode_paged_noalloc(const mla_decode_args* args, void* stream);
 
 /*
+ * mla_stream_read -- diagnostic: reads `bytes` (a multiple of 16) of device
+ * memory at src once with 16-byte loads and discards them, so that the
+ * caller can time the read bandwidth a plain stream reaches on this GPU (the
+ * reference against which the decode's cache-read rate is judged; the
+ * V2 analysis page, section 1.2, puts decode at the cache-read bound). sink
+ * (device, 16 bytes, 16-byte aligned) is written only in the rare case that
+ * the folded loads equal a fixed sentinel. Misaligned pointers or sizes
+ * return MLA_ERR_UNSUPPORTED.
+ */
+int mla_stream_read(const void* src, size_t bytes, void* sink, void* stream);
+
+/*
  * mla_out_proj -- each head's value up-projection applied after aggregation
  * (V2 analysis page, section 6.1: per-head aggregation first, then the head's
  * own matrix; the heads' matrices cannot be summed):

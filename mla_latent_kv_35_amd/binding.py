@@ -87,6 +87,8 @@ _lib.mla_decode_plan.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.POINTER(_i),
                                  ctypes.POINTER(_i), ctypes.POINTER(ctypes.c_size_t)]
 _lib.mla_decode_paged.restype = _i
 _lib.mla_decode_paged.argtypes = [ctypes.POINTER(DecodeArgs), _vp]
+_lib.mla_stream_read.restype = _i
+_lib.mla_stream_read.argtypes = [_vp, ctypes.c_size_t, _vp, _vp]
 _lib.mla_decode_paged_noalloc.restype = _i
 _lib.mla_decode_paged_noalloc.argtypes = [ctypes.POINTER(DecodeArgs), _vp]
 _lib.mla_rope_freq.restype = _i
@@ -109,7 +111,7 @@ _lib.mla_absorb_q_rope.argtypes = [_vp, _vp, _vp, _i, _i, _vp, _vp, _i, _vp, _i,
                                    _d, _vp, _vp]
 
 EXPORTED = ["mla_status_str", "mla_abi_version", "mla_absorb_q", "mla_rope",
-            "mla_decode_plan", "mla_decode_paged", "mla_decode_paged_noalloc", "mla_out_proj", "mla_cache_append",
+            "mla_decode_plan", "mla_decode_paged", "mla_decode_paged_noalloc", "mla_stream_read", "mla_out_proj", "mla_cache_append",
             "mla_rope_freq", "mla_yarn_frequencies", "mla_yarn_mscale", "mla_expand_kv",
             "mla_prefill_attn", "mla_absorb_q_rope"]
 
@@ -388,6 +390,12 @@ def decode_paged_noalloc(q_lat: torch.Tensor, q_rope: torch.Tensor, cache: Paged
     a.out, a.lse = _ptr(out), _ptr(lse)
     _check("mla_decode_paged_noalloc", _lib.mla_decode_paged_noalloc(ctypes.byref(a), _stream(stream)))
     return out, lse
+
+
+def stream_read(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Read all of src once on the device (the bandwidth probe; sink: 16 bytes)."""
+    _check("mla_stream_read", _lib.mla_stream_read(_ptr(src), src.numel() * src.element_size(),
+                                                   _ptr(sink), _stream(stream)))
 
 
 # ---------------------------------------------------------------------------

@@ -18,9 +18,9 @@ ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libmla.so")
 ARCH = "gfx950"
 
-SOURCES = ["mla_api.hip", "decode_pipe.hip", "decode_split.hip", "decode_mfma.hip", "decode_simple.hip", "combine.hip",
+SOURCES = ["mla_api.hip", "decode_pipe.hip", "decode_mfma.hip", "decode_simple.hip", "combine.hip",
            "rope.hip", "absorb.hip", "out_proj.hip", "append.hip", "prefill.hip",
-           "gemm_nt.hip"]
+           "gemm_nt.hip", "probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

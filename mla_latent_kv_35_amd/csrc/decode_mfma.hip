@@ -683,11 +683,6 @@ void decode_mfma_kernel(DecodeParams p) {
 
 }  // namespace
 
-hipError_t launch_decode_mfma_bf16(const DecodeParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(decode_mfma_kernel<false>, dim3(p.per_xcd * kNumXcd), dim3(kThreads), 0, s, p);
-  return hipGetLastError();
-}
-
 hipError_t launch_decode_mfma_fp8(const DecodeParams& p, hipStream_t s) {
   hipLaunchKernelGGL(decode_mfma_kernel<true>, dim3(p.per_xcd * kNumXcd), dim3(kThreads), 0, s, p);
   return hipGetLastError();

@@ -67,11 +67,8 @@ Plan make_plan(const mla_decode_args* a) {
   const int64_t total = a->total_tokens > 0 ? a->total_tokens : (int64_t)a->B * Lmax;
   const int64_t pages_total = (total + kPage - 1) / kPage;
   const int64_t max_pages = (Lmax + kPage - 1) / kPage;
-  // 128 rows per workgroup when the batch's row groups alone fill the GPU
-  // (each page is then read by one workgroup); else 64, whose two row groups
-  // of a sequence share every page through L2
-  if (a->ckv_dt == MLA_BF16 || (a->ckv_dt != MLA_F32 && (int64_t)a->B * ((R + 127) / 128) >= kNumCu))
-    pl.rows = 128;
+  // bf16 pools: 128 rows per workgroup (the pipelined kernel); fp8 pools: 64
+  if (a->ckv_dt == MLA_BF16) pl.rows = 128;
   pl.G = (int)((R + pl.rows - 1) / pl.rows);
   if (a->split_tokens > 0) {
     pl.split_tokens = a->split_tokens;
@@ -316,7 +313,7 @@ int mla_decode_paged(const mla_decode_args* a, void* stream) {
   hipError_t e;
   if (a->ckv_dt == MLA_F32) e = launch_decode_simple_f32(p, s);
   else if (a->ckv_dt == MLA_BF16) e = launch_decode_pipe(p, s);
-  else e = launch_decode_split(p, 1, pl.rows, s);
+  else e = launch_decode_mfma_fp8(p, s);
   if (e != hipSuccess) return MLA_ERR_LAUNCH;
   if (pl.n_split > 1) {
     CombineParams c{};
@@ -368,6 +365,13 @@ int mla_decode_paged_noalloc(const mla_decode_args* args, void* stream) {
   a.workspace = ws;
   a.workspace_bytes = MLA_NOALLOC_SCRATCH_BYTES;
   return mla_decode_paged(&a, stream);
+}
+
+int mla_stream_read(const void* src, size_t bytes, void* sink, void* stream) {
+  if (!src || !sink) return MLA_ERR_NULL;
+  if (bytes % 16 != 0 || (uintptr_t)src % 16 != 0 || (uintptr_t)sink % 16 != 0) return MLA_ERR_UNSUPPORTED;
+  if (bytes == 0) return MLA_OK;
+  return launch_stream_read(src, bytes, sink, (hipStream_t)stream) == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
 }
 
 int mla_out_proj(const void* u, const void* w_uv, void* o, int u_dt, int w_dt, int o_dt, int n_tok,

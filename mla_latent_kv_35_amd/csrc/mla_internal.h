@@ -65,12 +65,11 @@ struct CombineParams {
 
 
 
-hipError_t launch_decode_mfma_bf16(const DecodeParams& p, hipStream_t s);
 hipError_t launch_decode_mfma_fp8(const DecodeParams& p, hipStream_t s);
 hipError_t launch_decode_simple_f32(const DecodeParams& p, hipStream_t s);
 // fp8: E4M3FN latent pool with per-token scales; rows: query rows per workgroup (64 or 128)
-hipError_t launch_decode_split(const DecodeParams& p, int fp8, int rows, hipStream_t s);
 hipError_t launch_decode_pipe(const DecodeParams& p, hipStream_t s);
+hipError_t launch_stream_read(const void* src, size_t bytes, void* sink, hipStream_t s);
 hipError_t launch_combine(const CombineParams& p, hipStream_t s);
 // combine fused with the value up-projection; needs p.w_uv, p.o, n_split <= 64
 hipError_t launch_combine_out(const CombineParams& p, hipStream_t s);

@@ -194,3 +194,13 @@ def test_dense_entry_points_reject_misaligned_pointers(B):
     assert L.mla_expand_kv(fake, fake, fake, fake, odd, 0, 0, 0, 4, 8, 128, 512, None) == 4
     assert L.mla_absorb_q_rope(fake, fake, odd, 1, 1, fake, fake, 1, fake, 4, 8, 128, 512, 64,
                                1e4, None, None) == 4
+
+
+def test_stream_read_rejects_misaligned(B):
+    lib = B.lib()
+    # host-side checks only: no launch happens for these
+    assert lib.mla_stream_read(None, 16, 16, None) == 1    # MLA_ERR_NULL
+    assert lib.mla_stream_read(16, 24, 16, None) == 4      # size not a multiple of 16
+    assert lib.mla_stream_read(8, 16, 16, None) == 4       # src not 16-byte aligned
+    assert lib.mla_stream_read(16, 16, 8, None) == 4       # sink not 16-byte aligned
+    assert lib.mla_stream_read(16, 0, 16, None) == 0       # nothing to read

@@ -409,3 +409,11 @@ def test_graph_replay_matches_eager(mla):
             assert torch.equal(bufs[k].view(torch.int16) if bufs[k].dtype == torch.bfloat16 else bufs[k],
                                ref[k].view(torch.int16) if ref[k].dtype == torch.bfloat16 else ref[k]), (rep, k)
         del junk
+
+
+def test_stream_read_probe_runs(mla):
+    src = torch.ones(64 << 20, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    mla.stream_read(src, sink)
+    torch.cuda.synchronize()
+    assert int(sink.sum()) == 0       # the folded loads of all-ones bytes never hit the sentinel
