@@ -266,6 +266,17 @@ int mla_decode_paged_noalloc(const mla_decode_args* args, void* stream);
 int mla_stream_read(const void* src, size_t bytes, void* sink, void* stream);
 
 /*
+ * mla_set_wait_limit -- diagnostic: the number of polls (each followed by a
+ * short sleep) a bounded wait inside a decode kernel makes before it gives
+ * up; the fp8 kernel's waves wait so for their partner wave's tile maxima. A
+ * wait that gives up marks its work unit, whose outputs (u and lse, or its
+ * partials) become NaN, and the kernel exits normally. 0 makes every such
+ * wait give up at once (how the failure path is tested). Process-wide,
+ * default 1 << 20; returns the previous value, or -1 for a negative one.
+ */
+int mla_set_wait_limit(int polls);
+
+/*
  * mla_out_proj -- each head's value up-projection applied after aggregation
  * (V2 analysis page, section 6.1: per-head aggregation first, then the head's
  * own matrix; the heads' matrices cannot be summed):

@@ -202,6 +202,7 @@ void decode_mfma_kernel(DecodeParams p) {
   const int pg_end = (tok1 + kPage - 1) / kPage;
   const int n_tiles = (tok1 - tok0 + kTileTok - 1) / kTileTok;
   // sequence-level range checks; page ids are checked by the aggregation team
+  bool expired = false;                      // a partner wait gave up (see the step loop)
   const bool seq_bad = (L < p.T) || (L > p.max_seq_len) ||
                        ((L + kPage - 1) / kPage > p.max_pages) ||
                        (pg_end - pg_begin) > kMaxSplitPages;
@@ -379,10 +380,17 @@ void decode_mfma_kernel(DecodeParams p) {
         __builtin_amdgcn_s_waitcnt(0xC07F);
         asm volatile("" ::: "memory");
         if (lane == 0) *(volatile MLA_LDS int*)(flags + w) = j;
-        int it = 0;
-        while (__builtin_amdgcn_readfirstlane(*(volatile MLA_LDS int*)(flags + (w ^ 2))) != j &&
-               ++it < (1 << 20))
+        // bounded: a wait that gives up marks the unit, whose outputs then
+        // become NaN (a limit of 0 gives up at once)
+        bool arrived = false;
+        for (int it = 0; it < p.spin_limit; ++it) {
+          if (__builtin_amdgcn_readfirstlane(*(volatile MLA_LDS int*)(flags + (w ^ 2))) == j) {
+            arrived = true;
+            break;
+          }
           __builtin_amdgcn_s_sleep(1);
+        }
+        expired |= !arrived;
         asm volatile("" ::: "memory");
       }
       if (j < n_tiles) {
@@ -429,7 +437,12 @@ void decode_mfma_kernel(DecodeParams p) {
         mbuf[32 * hh + 16 + lane] = m_s[1];
       }
     }
-    lds_barrier();  // (Z) row sums and reference maxima published
+    // (Z) row sums and reference maxima published; a partner wait that gave
+    // up anywhere in the workgroup turns the unit's outputs into NaN
+    if (__syncthreads_or(expired)) {
+      write_uniform_result(p, b, k, g, __builtin_nanf(""));
+      return;
+    }
     if (stage_u(p)) lds_barrier();   // (W) the aggregation team's u staged
     return;
   }
@@ -620,7 +633,12 @@ void decode_mfma_kernel(DecodeParams p) {
     // tile j+1 must be resident at the next (X); tile j+2's copies may fly on
     wait_tile(more);
   }
-  lds_barrier();  // (Z) row sums and reference maxima published
+  // (Z) row sums and reference maxima published; a partner wait that gave
+  // up anywhere in the workgroup turns the unit's outputs into NaN
+  if (__syncthreads_or(expired)) {
+    write_uniform_result(p, b, k, g, __builtin_nanf(""));
+    return;
+  }
 
   // ---- finish: u = U / l, or partials (m, l, U or u) ------------------------
   const bool direct = p.n_split == 1;

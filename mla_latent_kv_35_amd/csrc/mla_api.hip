@@ -3,6 +3,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 
 #include "mla_extra.h"
@@ -99,6 +100,14 @@ Plan make_plan(const mla_decode_args* a) {
   return pl;
 }
 
+}  // namespace
+}  // namespace mla
+
+// Polls a bounded in-kernel wait makes before it gives up (and the unit's
+// outputs become NaN); changed only through mla_set_wait_limit.
+namespace mla {
+namespace {
+std::atomic<int> g_spin_limit{1 << 20};
 }  // namespace
 }  // namespace mla
 
@@ -304,6 +313,7 @@ int mla_decode_paged(const mla_decode_args* a, void* stream) {
   p.max_seq_len = a->max_seq_len;
   p.out_bf16 = a->out_dt == MLA_BF16;
   p.scale_log2 = a->softmax_scale * kLog2e;
+  p.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
   const int64_t units = (int64_t)a->B * pl.n_split * pl.G;
   if (units > (int64_t)1 << 30) return MLA_ERR_UNSUPPORTED;
   p.n_units = (int)units;
@@ -365,6 +375,11 @@ int mla_decode_paged_noalloc(const mla_decode_args* args, void* stream) {
   a.workspace = ws;
   a.workspace_bytes = MLA_NOALLOC_SCRATCH_BYTES;
   return mla_decode_paged(&a, stream);
+}
+
+int mla_set_wait_limit(int polls) {
+  if (polls < 0) return -1;
+  return g_spin_limit.exchange(polls);
 }
 
 int mla_stream_read(const void* src, size_t bytes, void* sink, void* stream) {

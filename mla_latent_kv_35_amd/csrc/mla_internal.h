@@ -42,6 +42,7 @@ struct DecodeParams {
   int n_units;              // work units actually present
   int per_xcd;              // grid = per_xcd * 8 (XCD-major unit numbering)
   float scale_log2;         // softmax_scale * log2(e)
+  int spin_limit;           // polls of a bounded wait before it gives up (fp8 kernel)
 };
 
 struct CombineParams {

@@ -204,3 +204,12 @@ def test_stream_read_rejects_misaligned(B):
     assert lib.mla_stream_read(8, 16, 16, None) == 4       # src not 16-byte aligned
     assert lib.mla_stream_read(16, 16, 8, None) == 4       # sink not 16-byte aligned
     assert lib.mla_stream_read(16, 0, 16, None) == 0       # nothing to read
+
+
+def test_wait_limit_setter(B):
+    lib = B.lib()
+    prev = lib.mla_set_wait_limit(12345)
+    assert prev == 1 << 20
+    assert lib.mla_set_wait_limit(prev) == 12345
+    assert lib.mla_set_wait_limit(-1) == -1
+    assert lib.mla_set_wait_limit(prev) == prev

@@ -209,6 +209,11 @@ def test_ragged_full_sampled(mla):
     check_against_oracle(mla, inp, batches=pick)
 
 
+def test_ragged_full_all_sequences(mla):
+    # every one of the 64 ragged sequences against the oracle, row by row
+    check_against_oracle(mla, synth.make_inputs("ragged"))
+
+
 def test_long_128k_full(mla):
     check_against_oracle(mla, synth.make_inputs("long_128k"))
 
@@ -220,6 +225,11 @@ def test_mtp_fp8_full_sampled(mla):
     rng = np.random.default_rng(78)
     pick = sorted(set([0, inp.cfg.B - 1] + rng.choice(inp.cfg.B, 6, replace=False).tolist()))
     check_against_oracle(mla, inp, batches=pick)
+
+
+def test_mtp_fp8_full_all_sequences(mla):
+    # all 128 two-token sequences of the fp8 workload against the oracle
+    check_against_oracle(mla, synth.make_inputs("mtp_fp8"))
 
 
 # --------------------------------------------------------------------------
@@ -417,3 +427,26 @@ def test_stream_read_probe_runs(mla):
     mla.stream_read(src, sink)
     torch.cuda.synchronize()
     assert int(sink.sum()) == 0       # the folded loads of all-ones bytes never hit the sentinel
+
+
+def test_fp8_partner_wait_gives_up_loudly(mla):
+    """The fp8 kernel's bounded partner wait: with a limit of 0 every wait
+    gives up, every unit's outputs turn NaN and the kernels exit normally;
+    with the limit restored the same call is correct again."""
+    cfg = synth.small_config(B=2, H=64, T=1, seq_len=300, ckv_dt="fp8", seed=91)
+    inp = synth.make_inputs(cfg)
+    d = mla.upload(inp)
+    q_lat = mla.absorb_q(d.q_nope, d.w_uk)
+    q_rot = mla.rope(d.q_rope, d.positions)
+    for split in (0, 64):
+        prev = mla.set_wait_limit(0)
+        try:
+            u, lse = mla.decode_paged(q_lat, q_rot, d.cache, 1, d.softmax_scale, split_tokens=split)
+            torch.cuda.synchronize()
+        finally:
+            mla.set_wait_limit(prev)
+        assert torch.isnan(u.float()).all() and torch.isnan(lse).all(), split
+        u2, _ = mla.decode_paged(q_lat, q_rot, d.cache, 1, d.softmax_scale, split_tokens=split)
+        torch.cuda.synchronize()
+        ref = O.decode_step(inp)
+        assert row_rel(host(u2), np.stack([ref[b]["u"][0] for b in ref])) <= TOL["fp8"]
