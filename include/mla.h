@@ -11,9 +11,14 @@
  * latents u = sum_s a_s c_s, and only then applies its own W^UV (section 6.1).
  *
  * Conventions for every entry point:
- *  - Tensor pointers are DEVICE pointers, owned by the caller, contiguous in
- *    the layout stated (row-major, last index fastest). The library never
- *    allocates, frees or keeps a pointer after the call returns.
+ *  - Tensor pointers are DEVICE pointers, owned by the caller, in the
+ *    layout stated (row-major, last index fastest). Where a call takes
+ *    strides they count ELEMENTS, 0 selects the packed layout, and a "row"
+ *    is the innermost vector of one (token, head) pair: a [n][H][d] tensor
+ *    with row stride r holds element (n, h, i) at (n * H + h) * r + i, so
+ *    a slice of a wider per-head vector (say the first 128 of each head's
+ *    192 query elements) is passed as-is. The library never allocates,
+ *    frees or keeps a pointer after the call returns.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = default stream) and
  *    is stream-ordered; the library never synchronizes.
  *  - Arguments are checked on the host before anything is launched; a bad
@@ -24,7 +29,9 @@
  *    page ids are out of range gets NaN outputs instead of a memory fault.
  *  - Results are deterministic: no atomics, fixed reduction order; the
  *    order depends on logical token indices only, never on physical pages.
- *  - There is no global mutable state; calls are thread-safe.
+ *  - Calls are thread-safe. The only process-wide state is the diagnostic
+ *    wait limit (mla_set_wait_limit) and the static array of the
+ *    allocation-free decode entry point.
  *
  * dtypes: MLA_F32 = IEEE binary32, MLA_BF16 = bfloat16, MLA_FP8_E4M3 = OCP
  * E4M3FN (bias 7, max 448, no infinities) with one fp32 scale per token.
@@ -39,7 +46,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 1
+#define MLA_ABI_VERSION 2
 #define MLA_PAGE_SIZE 64
 
 typedef enum {
@@ -66,16 +73,21 @@ int mla_abi_version(void);
  * i.e. q^T (W^UK c) = (W^UK^T q)^T c (V2 analysis page, section 1.2 and the
  * first absorption condition of section 6: a fixed linear map moved to the
  * query side).
- *   q_nope : [n_tok][H][d_h]  dtype q_dt (F32 or BF16)
- *   w_uk   : [H][d_h][d_c]    dtype q_dt (head h's up-projection, d_h x d_c)
- *   q_lat  : [n_tok][H][d_c]  dtype out_dt (F32, or BF16 when q_dt is BF16)
+ *   q_nope : [n_tok][H][d_h]  dtype q_dt (F32 or BF16), row stride
+ *            q_row_stride (0: d_h)
+ *   w_uk   : [H][d_h][d_c]    dtype q_dt (head h's up-projection, d_h x d_c),
+ *            packed
+ *   q_lat  : [n_tok][H][d_c]  dtype out_dt (F32, or BF16 when q_dt is BF16),
+ *            row stride out_row_stride (0: d_c)
  * Supported: d_h = 128, d_c = 512, n_tok >= 0 (0 launches nothing), H >= 1,
- * 16-byte aligned tensors (else MLA_ERR_UNSUPPORTED).
+ * 16-byte aligned tensors and rows (row stride x element size a multiple of
+ * 16 bytes; else MLA_ERR_UNSUPPORTED). A row stride that is negative or
+ * below the row length is MLA_ERR_SHAPE.
  * Accumulation is fp32; F32 inputs use fp32 FMA end to end.
  */
 int mla_absorb_q(const void* q_nope, const void* w_uk, void* q_lat,
                  int q_dt, int out_dt, int n_tok, int H, int d_h, int d_c,
-                 void* stream);
+                 int64_t q_row_stride, int64_t out_row_stride, void* stream);
 
 /*
  * mla_rope -- rotary position embedding of the decoupled rope query or key.
@@ -85,22 +97,34 @@ int mla_absorb_q(const void* q_nope, const void* w_uk, void* q_lat,
  *   a = pos[n] * base^(-2i/d_r)           (angle in fp64)
  *   y[2i]   = x[2i] cos a - x[2i+1] sin a
  *   y[2i+1] = x[2i] sin a + x[2i+1] cos a
- *   x_in, x_out : [n_tok][n_heads][d_r], dtype dt (F32 or BF16); may alias
- *                 exactly (in place)
+ *   x_in, x_out : [n_tok][n_heads][d_r], dtype dt (F32 or BF16); element
+ *                 (n, h, i) of x_in at n * in_tok_stride +
+ *                 h * in_head_stride + i, of x_out likewise with the out
+ *                 strides (0: the packed n_heads * d_r and d_r). They are
+ *                 disjoint, or the same memory with the same strides
+ *                 (in place); x_out's vectors must not overlap one another.
  *   pos         : int32 [n_tok], positions >= 0
- * Supported: d_r even, 2 <= d_r <= 256; n_tok >= 0.
+ * Supported: d_r even, 2 <= d_r <= 256; n_tok >= 0; any strides >= 0 (a
+ * stride that is negative, or an out stride that makes output vectors
+ * overlap, is MLA_ERR_SHAPE; x_in == x_out with different strides is too).
+ * d_r = 64 with 16-byte aligned vectors takes a vectorised kernel.
  */
 int mla_rope(const void* x_in, void* x_out, int dt, const int32_t* pos,
-             int n_tok, int n_heads, int d_r, double base, void* stream);
+             int n_tok, int n_heads, int d_r, double base,
+             int64_t in_tok_stride, int64_t in_head_stride,
+             int64_t out_tok_stride, int64_t out_head_stride, void* stream);
 
 /*
  * mla_rope_freq -- mla_rope with caller-given per-pair frequencies:
  *   a = pos[n] * theta[i]   (fp64), then the same rotation as mla_rope.
  *   theta : DEVICE fp64 [d_r / 2], e.g. from mla_yarn_frequencies.
- * Same layouts, support and errors as mla_rope (theta NULL: MLA_ERR_NULL).
+ * Same layouts, strides, support and errors as mla_rope (theta NULL:
+ * MLA_ERR_NULL).
  */
 int mla_rope_freq(const void* x_in, void* x_out, int dt, const int32_t* pos,
-                  int n_tok, int n_heads, int d_r, const double* theta, void* stream);
+                  int n_tok, int n_heads, int d_r, const double* theta,
+                  int64_t in_tok_stride, int64_t in_head_stride,
+                  int64_t out_tok_stride, int64_t out_head_stride, void* stream);
 
 /*
  * mla_absorb_q_rope -- the query side of a decode step in one call: the
@@ -112,8 +136,12 @@ int mla_rope_freq(const void* x_in, void* x_out, int dt, const int32_t* pos,
  * independent, so with queries and rope data both BF16 or both F32, d_r = 64
  * and 16-byte aligned rope rows they run as one kernel launch; otherwise as
  * the two calls.
- *   q_nope, w_uk, q_lat, q_dt, out_dt, d_h, d_c : as mla_absorb_q (n_tok x H)
- *   q_rope, q_rot : [n_tok][H][d_r], dtype rope_dt (F32 or BF16); may alias
+ *   q_nope, w_uk, q_lat, q_dt, out_dt, d_h, d_c, q_row_stride,
+ *   out_row_stride : as mla_absorb_q (n_tok x H)
+ *   q_rope, q_rot : [n_tok][H][d_r], dtype rope_dt (F32 or BF16), row
+ *                   strides rope_row_stride and rot_row_stride (0: d_r;
+ *                   mla_rope's token and head strides H * r and r); in place
+ *                   when the same memory with the same stride
  *   pos           : int32 [n_tok]
  *   theta         : DEVICE fp64 [d_r / 2] or NULL (then base^(-2i/d_r))
  * Errors: those of mla_absorb_q and mla_rope / mla_rope_freq; nothing is
@@ -122,7 +150,8 @@ int mla_rope_freq(const void* x_in, void* x_out, int dt, const int32_t* pos,
 int mla_absorb_q_rope(const void* q_nope, const void* w_uk, void* q_lat, int q_dt, int out_dt,
                       const void* q_rope, void* q_rot, int rope_dt, const int32_t* pos,
                       int n_tok, int H, int d_h, int d_c, int d_r, double base,
-                      const double* theta, void* stream);
+                      const double* theta, int64_t q_row_stride, int64_t out_row_stride,
+                      int64_t rope_row_stride, int64_t rot_row_stride, void* stream);
 
 /*
  * mla_yarn_frequencies -- YaRN frequencies of the decoupled rope part for a
@@ -184,7 +213,13 @@ typedef struct mla_decode_args {
                                tokens [k*split_tokens, (k+1)*split_tokens) */
   int64_t total_tokens;     /* host hint: sum of seq_lens (0 = unknown) */
   float softmax_scale;      /* 1/sqrt(d_h + d_r) for DeepSeek-V2 (eq. 18) */
-  int32_t reserved0;        /* must be 0 */
+  int32_t heads_per_wg;     /* query rows (token, head pairs) per workgroup:
+                               0 = the kernel's own (BF16 pools 128, FP8 64,
+                               F32 1; mla_decode_plan reports it), else it
+                               must equal that value (MLA_ERR_UNSUPPORTED) */
+  int64_t q_lat_stride;     /* row stride of q_lat (0: d_c), >= d_c */
+  int64_t q_rope_stride;    /* row stride of q_rope (0: d_r), >= d_r; both
+                               with rows 16-byte aligned */
   const void* q_lat;        /* [B][T][H][d_c] absorbed queries (mla_absorb_q) */
   const void* q_rope;       /* [B][T][H][d_r] rotated rope queries (mla_rope) */
   const void* ckv;          /* [n_pages][64][d_c] latent pool */
@@ -211,16 +246,17 @@ typedef struct mla_decode_args {
 } mla_decode_args;
 
 /*
- * mla_decode_plan -- host-only: the split size, split count and workspace
- * bytes mla_decode_paged will use for these arguments (pointers may be NULL).
- * With more than one split, each (sequence, split, 64-row group) produces
+ * mla_decode_plan -- host-only: the split size, split count, query rows per
+ * workgroup and workspace bytes mla_decode_paged will use for these
+ * arguments (pointers may be NULL; any output pointer may be NULL).
+ * With more than one split, each (sequence, split, row group) produces
  * partials merged by a log-sum-exp combine kernel: fp32 (m, l) per row and
  * the split's latent aggregate, as fp32 U when out_dt is F32 and as bf16
  * u = U / l when out_dt is BF16 (bf16 and fp8 pools), so the workspace size
  * depends on out_dt.
  */
 int mla_decode_plan(const mla_decode_args* args, int* split_tokens, int* n_split,
-                    size_t* workspace_bytes);
+                    int* heads_per_wg, size_t* workspace_bytes);
 
 /*
  * mla_decode_paged -- absorbed MLA decode over the paged cache (V2 analysis
@@ -281,14 +317,19 @@ int mla_set_wait_limit(int polls);
  * (V2 analysis page, section 6.1: per-head aggregation first, then the head's
  * own matrix; the heads' matrices cannot be summed):
  *   o[n][h][:] = W_UV[h] u[n][h][:]
- *   u    : [n_tok][H][d_c]  dtype u_dt (F32 or BF16)
- *   w_uv : [H][d_h][d_c]    dtype w_dt (F32 or BF16; F32 requires u_dt F32)
- *   o    : [n_tok][H][d_h]  dtype o_dt (F32 or BF16)
- * Supported: d_h = 128, d_c = 512, 16-byte aligned tensors (else
- * MLA_ERR_UNSUPPORTED). fp32 accumulation.
+ *   u    : [n_tok][H][d_c]  dtype u_dt (F32 or BF16), row stride
+ *          u_row_stride (0: d_c)
+ *   w_uv : [H][d_h][d_c]    dtype w_dt (F32 or BF16; F32 requires u_dt F32),
+ *          packed
+ *   o    : [n_tok][H][d_h]  dtype o_dt (F32 or BF16), row stride
+ *          o_row_stride (0: d_h)
+ * Supported: d_h = 128, d_c = 512, 16-byte aligned tensors and rows (else
+ * MLA_ERR_UNSUPPORTED); a row stride that is negative or below the row
+ * length is MLA_ERR_SHAPE. fp32 accumulation.
  */
 int mla_out_proj(const void* u, const void* w_uv, void* o, int u_dt, int w_dt,
-                 int o_dt, int n_tok, int H, int d_h, int d_c, void* stream);
+                 int o_dt, int n_tok, int H, int d_h, int d_c, int64_t u_row_stride,
+                 int64_t o_row_stride, void* stream);
 
 /*
  * Arguments of the cache append: the step that puts each new token's cache

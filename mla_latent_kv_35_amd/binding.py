@@ -47,7 +47,8 @@ class DecodeArgs(ctypes.Structure):
         ("q_dt", ctypes.c_int32), ("ckv_dt", ctypes.c_int32), ("kr_dt", ctypes.c_int32),
         ("out_dt", ctypes.c_int32), ("split_tokens", ctypes.c_int32),
         ("total_tokens", ctypes.c_int64),
-        ("softmax_scale", ctypes.c_float), ("reserved0", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float), ("heads_per_wg", ctypes.c_int32),
+        ("q_lat_stride", ctypes.c_int64), ("q_rope_stride", ctypes.c_int64),
         ("q_lat", ctypes.c_void_p), ("q_rope", ctypes.c_void_p),
         ("ckv", ctypes.c_void_p), ("kr", ctypes.c_void_p), ("ckv_scale", ctypes.c_void_p),
         ("block_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
@@ -74,17 +75,18 @@ class AppendArgs(ctypes.Structure):
     ]
 
 
-_vp, _i, _d = ctypes.c_void_p, ctypes.c_int, ctypes.c_double
+_vp, _i, _d, _l = ctypes.c_void_p, ctypes.c_int, ctypes.c_double, ctypes.c_int64
 _lib.mla_status_str.restype = ctypes.c_char_p
 _lib.mla_status_str.argtypes = [_i]
 _lib.mla_abi_version.restype = _i
 _lib.mla_absorb_q.restype = _i
-_lib.mla_absorb_q.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]
+_lib.mla_absorb_q.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _l, _l, _vp]
 _lib.mla_rope.restype = _i
-_lib.mla_rope.argtypes = [_vp, _vp, _i, _vp, _i, _i, _i, _d, _vp]
+_lib.mla_rope.argtypes = [_vp, _vp, _i, _vp, _i, _i, _i, _d, _l, _l, _l, _l, _vp]
 _lib.mla_decode_plan.restype = _i
 _lib.mla_decode_plan.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.POINTER(_i),
-                                 ctypes.POINTER(_i), ctypes.POINTER(ctypes.c_size_t)]
+                                 ctypes.POINTER(_i), ctypes.POINTER(_i),
+                                 ctypes.POINTER(ctypes.c_size_t)]
 _lib.mla_decode_paged.restype = _i
 _lib.mla_decode_paged.argtypes = [ctypes.POINTER(DecodeArgs), _vp]
 _lib.mla_set_wait_limit.restype = _i
@@ -94,7 +96,7 @@ _lib.mla_stream_read.argtypes = [_vp, ctypes.c_size_t, _vp, _vp]
 _lib.mla_decode_paged_noalloc.restype = _i
 _lib.mla_decode_paged_noalloc.argtypes = [ctypes.POINTER(DecodeArgs), _vp]
 _lib.mla_rope_freq.restype = _i
-_lib.mla_rope_freq.argtypes = [_vp, _vp, _i, _vp, _i, _i, _i, _vp, _vp]
+_lib.mla_rope_freq.argtypes = [_vp, _vp, _i, _vp, _i, _i, _i, _vp, _l, _l, _l, _l, _vp]
 _lib.mla_yarn_frequencies.restype = _i
 _lib.mla_yarn_frequencies.argtypes = [_i, _d, _d, _d, _d, _i, ctypes.POINTER(_d)]
 _lib.mla_yarn_mscale.restype = _d
@@ -107,10 +109,10 @@ _lib.mla_prefill_attn.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i,
 _lib.mla_cache_append.restype = _i
 _lib.mla_cache_append.argtypes = [ctypes.POINTER(AppendArgs), _vp]
 _lib.mla_out_proj.restype = _i
-_lib.mla_out_proj.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]
+_lib.mla_out_proj.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _l, _l, _vp]
 _lib.mla_absorb_q_rope.restype = _i
 _lib.mla_absorb_q_rope.argtypes = [_vp, _vp, _vp, _i, _i, _vp, _vp, _i, _vp, _i, _i, _i, _i, _i,
-                                   _d, _vp, _vp]
+                                   _d, _vp, _l, _l, _l, _l, _vp]
 
 EXPORTED = ["mla_status_str", "mla_abi_version", "mla_absorb_q", "mla_rope",
             "mla_decode_plan", "mla_decode_paged", "mla_decode_paged_noalloc", "mla_stream_read",
@@ -155,31 +157,71 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return t.data_ptr()
 
 
+def _row_stride(t: torch.Tensor) -> int:
+    """Row stride of a [n, H, d] view whose (token, head) rows are evenly
+    spaced: strides (H * r, r, 1), e.g. a slice of the last dimension of a
+    wider contiguous tensor."""
+    if t.dim() != 3:
+        raise ValueError("expected a 3-d tensor")
+    n, H, d = t.shape
+    s0, s1, s2 = t.stride()
+    if d > 1 and s2 != 1:
+        raise ValueError("the last dimension must be unit-stride")
+    if H == 1:
+        s1 = s0 if n > 1 else d
+    if n > 1 and s0 != H * s1:
+        raise ValueError("rows must be evenly spaced: stride(0) == H * stride(1)")
+    return s1
+
+
+def _rows(t: torch.Tensor):
+    """(device pointer, row stride) of a [n, H, d] view (see _row_stride)."""
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    return t.data_ptr(), _row_stride(t)
+
+
+def _vecs(t: torch.Tensor):
+    """(pointer, token stride, head stride) of a [n, heads, d] device view with
+    a unit-stride last dimension."""
+    if not t.is_cuda or t.dim() != 3:
+        raise ValueError("expected a 3-d device tensor")
+    if t.shape[2] > 1 and t.stride(2) != 1:
+        raise ValueError("the last dimension must be unit-stride")
+    return t.data_ptr(), t.stride(0), t.stride(1)
+
+
 # ---------------------------------------------------------------------------
 # entry points (one function per C call)
 # ---------------------------------------------------------------------------
 
 def absorb_q(q_nope: torch.Tensor, w_uk: torch.Tensor, out_dtype=None,
              out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """q_lat[n,h,:] = W_UK[h]^T q_nope[n,h,:]; q_nope [n,H,128], w_uk [H,128,512]."""
+    """q_lat[n,h,:] = W_UK[h]^T q_nope[n,h,:]; q_nope [n,H,128] (rows may be
+    strided, e.g. a slice of [n,H,192]), w_uk [H,128,512]."""
     n, H, dh = q_nope.shape
     dc = w_uk.shape[2]
     if out is None:
         out = torch.empty((n, H, dc), dtype=out_dtype or q_nope.dtype, device=q_nope.device)
-    _check("mla_absorb_q", _lib.mla_absorb_q(_ptr(q_nope), _ptr(w_uk), _ptr(out),
-                                             dtype_code(q_nope), dtype_code(out), n, H, dh, dc,
+    qp, qs = _rows(q_nope)
+    op, os_ = _rows(out)
+    _check("mla_absorb_q", _lib.mla_absorb_q(qp, _ptr(w_uk), op, dtype_code(q_nope),
+                                             dtype_code(out), n, H, dh, dc, qs, os_,
                                              _stream(stream)))
     return out
 
 
 def rope(x: torch.Tensor, pos: torch.Tensor, base: float = 10000.0,
          out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """Rotate pairs (2i, 2i+1) of x [n, heads, d_r] at positions pos [n] (int32)."""
+    """Rotate pairs (2i, 2i+1) of x [n, heads, d_r] at positions pos [n] (int32);
+    x and out may be strided views (unit-stride last dimension)."""
     n, heads, dr = x.shape
     if out is None:
-        out = torch.empty_like(x)
-    _check("mla_rope", _lib.mla_rope(_ptr(x), _ptr(out), dtype_code(x), _ptr(pos), n, heads, dr,
-                                     float(base), _stream(stream)))
+        out = torch.empty((n, heads, dr), dtype=x.dtype, device=x.device)
+    xp, xt, xh = _vecs(x)
+    yp, yt, yh = _vecs(out)
+    _check("mla_rope", _lib.mla_rope(xp, yp, dtype_code(x), _ptr(pos), n, heads, dr, float(base),
+                                     xt, xh, yt, yh, _stream(stream)))
     return out
 
 
@@ -188,10 +230,12 @@ def rope_freq(x: torch.Tensor, pos: torch.Tensor, theta: torch.Tensor,
     """mla_rope with per-pair frequencies theta (device float64 [d_r/2])."""
     n, heads, dr = x.shape
     if out is None:
-        out = torch.empty_like(x)
+        out = torch.empty((n, heads, dr), dtype=x.dtype, device=x.device)
     assert theta.dtype == torch.float64 and theta.numel() == dr // 2
-    _check("mla_rope_freq", _lib.mla_rope_freq(_ptr(x), _ptr(out), dtype_code(x), _ptr(pos), n,
-                                               heads, dr, _ptr(theta), _stream(stream)))
+    xp, xt, xh = _vecs(x)
+    yp, yt, yh = _vecs(out)
+    _check("mla_rope_freq", _lib.mla_rope_freq(xp, yp, dtype_code(x), _ptr(pos), n, heads, dr,
+                                               _ptr(theta), xt, xh, yt, yh, _stream(stream)))
     return out
 
 
@@ -207,13 +251,16 @@ def absorb_q_rope(q_nope: torch.Tensor, w_uk: torch.Tensor, q_rope: torch.Tensor
     if q_lat is None:
         q_lat = torch.empty((n, H, dc), dtype=out_dtype or q_nope.dtype, device=q_nope.device)
     if q_rot is None:
-        q_rot = torch.empty_like(q_rope)
+        q_rot = torch.empty((n, H, dr), dtype=q_rope.dtype, device=q_rope.device)
     if theta is not None:
         assert theta.dtype == torch.float64 and theta.numel() == dr // 2
+    qp, qs = _rows(q_nope)
+    lp, ls = _rows(q_lat)
+    rp, rs = _rows(q_rope)
+    tp, ts = _rows(q_rot)
     _check("mla_absorb_q_rope", _lib.mla_absorb_q_rope(
-        _ptr(q_nope), _ptr(w_uk), _ptr(q_lat), dtype_code(q_nope), dtype_code(q_lat),
-        _ptr(q_rope), _ptr(q_rot), dtype_code(q_rope), _ptr(pos), n, H, dh, dc, dr, float(base),
-        _ptr(theta), _stream(stream)))
+        qp, _ptr(w_uk), lp, dtype_code(q_nope), dtype_code(q_lat), rp, tp, dtype_code(q_rope),
+        _ptr(pos), n, H, dh, dc, dr, float(base), _ptr(theta), qs, ls, rs, ts, _stream(stream)))
     return q_lat, q_rot
 
 
@@ -264,13 +311,16 @@ def yarn_mscale(factor: float = 40.0, coef: float = 0.0707) -> float:
 
 def out_proj(u: torch.Tensor, w_uv: torch.Tensor, out_dtype=None,
              out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """o[n,h,:] = W_UV[h] u[n,h,:]; u [n,H,512], w_uv [H,128,512]."""
+    """o[n,h,:] = W_UV[h] u[n,h,:]; u [n,H,512], w_uv [H,128,512] (u and out
+    may have strided rows)."""
     n, H, dc = u.shape
     dh = w_uv.shape[1]
     if out is None:
         out = torch.empty((n, H, dh), dtype=out_dtype or w_uv.dtype, device=u.device)
-    _check("mla_out_proj", _lib.mla_out_proj(_ptr(u), _ptr(w_uv), _ptr(out), dtype_code(u),
-                                             dtype_code(w_uv), dtype_code(out), n, H, dh, dc,
+    up, us = _rows(u)
+    op, os_ = _rows(out)
+    _check("mla_out_proj", _lib.mla_out_proj(up, _ptr(w_uv), op, dtype_code(u), dtype_code(w_uv),
+                                             dtype_code(out), n, H, dh, dc, us, os_,
                                              _stream(stream)))
     return out
 
@@ -314,7 +364,9 @@ def make_decode_args(q_lat, q_rope, cache: PagedCache, T: int, softmax_scale: fl
     a.split_tokens = split_tokens
     a.total_tokens = int(cache.total_tokens)
     a.softmax_scale = softmax_scale
-    a.reserved0 = 0
+    a.heads_per_wg = 0
+    a.q_lat_stride = _row_stride(q_lat)
+    a.q_rope_stride = _row_stride(q_rope)
     return a
 
 
@@ -340,10 +392,18 @@ def cache_append(cache: PagedCache, c_in: torch.Tensor, k_in: torch.Tensor, seq:
 
 
 def decode_plan(args: DecodeArgs):
-    st, ns, ws = ctypes.c_int(), ctypes.c_int(), ctypes.c_size_t()
+    """(split_tokens, n_split, workspace_bytes) of mla_decode_plan."""
+    st, ns, _, ws = decode_plan_full(args)
+    return st, ns, ws
+
+
+def decode_plan_full(args: DecodeArgs):
+    """(split_tokens, n_split, heads_per_wg, workspace_bytes) of mla_decode_plan."""
+    st, ns, hw, ws = ctypes.c_int(), ctypes.c_int(), ctypes.c_int(), ctypes.c_size_t()
     _check("mla_decode_plan", _lib.mla_decode_plan(ctypes.byref(args), ctypes.byref(st),
-                                                   ctypes.byref(ns), ctypes.byref(ws)))
-    return st.value, ns.value, ws.value
+                                                   ctypes.byref(ns), ctypes.byref(hw),
+                                                   ctypes.byref(ws)))
+    return st.value, ns.value, hw.value, ws.value
 
 
 def decode_paged(q_lat: torch.Tensor, q_rope: torch.Tensor, cache: PagedCache, T: int,
@@ -364,7 +424,7 @@ def decode_paged(q_lat: torch.Tensor, q_rope: torch.Tensor, cache: PagedCache, T
     _, _, ws = decode_plan(a)
     if ws and (workspace is None or workspace.numel() < ws):
         workspace = torch.empty(ws, dtype=torch.uint8, device=q_lat.device)
-    a.q_lat, a.q_rope = _ptr(q_lat), _ptr(q_rope)
+    a.q_lat, a.q_rope = _rows(q_lat)[0], _rows(q_rope)[0]
     a.ckv, a.kr, a.ckv_scale = _ptr(cache.ckv), _ptr(cache.kr), _ptr(cache.ckv_scale)
     a.block_table, a.seq_lens = _ptr(cache.block_table), _ptr(cache.seq_lens)
     a.out, a.lse = _ptr(out), _ptr(lse)
@@ -387,7 +447,7 @@ def decode_paged_noalloc(q_lat: torch.Tensor, q_rope: torch.Tensor, cache: Paged
     the library's static per-device array, so the call allocates nothing
     (out and lse are the caller's)."""
     a = make_decode_args(q_lat, q_rope, cache, T, softmax_scale, out, lse, None, split_tokens)
-    a.q_lat, a.q_rope = _ptr(q_lat), _ptr(q_rope)
+    a.q_lat, a.q_rope = _rows(q_lat)[0], _rows(q_rope)[0]
     a.ckv, a.kr, a.ckv_scale = _ptr(cache.ckv), _ptr(cache.kr), _ptr(cache.ckv_scale)
     a.block_table, a.seq_lens = _ptr(cache.block_table), _ptr(cache.seq_lens)
     a.out, a.lse = _ptr(out), _ptr(lse)

@@ -8,7 +8,9 @@
 // transposed (ds_read_b64_tr_b16) as the K-major MFMA operand; the workgroup
 // then walks the tokens in blocks of 32, staging each block's queries in LDS
 // (double-buffered, the next block's loads in flight during the current
-// block's MFMAs) as the other operand. fp32: plain fp32 FMA.
+// block's MFMAs) as the other operand. fp32: plain fp32 FMA. Query row
+// (n, h) starts at (n * H + h) * q_rs elements, output row at
+// (n * H + h) * o_rs (packed: 128 and 512).
 #include "mla_device.h"
 #include "mla_extra.h"
 #include "mla_internal.h"
@@ -32,9 +34,10 @@ __device__ __forceinline__ int q_chunk(int t, int c) { return c ^ (t & 15); }
 
 template <bool OUT_BF16>
 __device__ __forceinline__ void absorb_bf16_block(int bid, lds_char* smem,
-                                                  const uint16_t* __restrict__ q,
+                                                  const uint16_t* __restrict__ q, long q_rs,
                                                   const uint16_t* __restrict__ wuk,
-                                                  void* __restrict__ out, int n_tok, int H) {
+                                                  void* __restrict__ out, long o_rs, int n_tok,
+                                                  int H) {
   // blocks on XCD x (= bid % 8) serve the heads h with h % 8 == x
   const int x = bid % kNumXcd, idx = bid / kNumXcd;
   const int h = kNumXcd * (idx >> 2) + x;
@@ -53,7 +56,7 @@ __device__ __forceinline__ void absorb_bf16_block(int bid, lds_char* smem,
       const int e = tid + kThreads * i, t = e >> 4, c = e & 15;
       const int n = tb * kTokTile + t;
       qv[i] = (u32x4_t){0u, 0u, 0u, 0u};
-      if (n < n_tok) qv[i] = *(const u32x4_t*)(q + ((size_t)n * H + h) * kDh + 8 * c);
+      if (n < n_tok) qv[i] = *(const u32x4_t*)(q + ((size_t)n * H + h) * q_rs + 8 * c);
     }
   };
   auto store_q = [&](int buf) __attribute__((always_inline)) {
@@ -122,7 +125,7 @@ __device__ __forceinline__ void absorb_bf16_block(int bid, lds_char* smem,
         for (int i = 0; i < 4; ++i) {
           const int n = n0 + 16 * tt + 4 * G4 + i;
           if (n < n_tok) {
-            const size_t o = ((size_t)n * H + h) * kDc + d;
+            const size_t o = ((size_t)n * H + h) * o_rs + d;
             if (OUT_BF16) ((uint16_t*)out)[o] = f2bf(acc[i]);
             else ((float*)out)[o] = acc[i];
           }
@@ -138,11 +141,12 @@ __device__ __forceinline__ void absorb_bf16_block(int bid, lds_char* smem,
 
 template <bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) void absorb_bf16_kernel(const uint16_t* __restrict__ q,
+                                                               long q_rs,
                                                                const uint16_t* __restrict__ wuk,
-                                                               void* __restrict__ out, int n_tok,
-                                                               int H) {
+                                                               void* __restrict__ out, long o_rs,
+                                                               int n_tok, int H) {
   __shared__ __attribute__((aligned(16))) char smem[kAbsorbLds];
-  absorb_bf16_block<OUT_BF16>(blockIdx.x, (lds_char*)smem, q, wuk, out, n_tok, H);
+  absorb_bf16_block<OUT_BF16>(blockIdx.x, (lds_char*)smem, q, q_rs, wuk, out, o_rs, n_tok, H);
 }
 
 // The query side of one decode step in one launch: the first n_abs blocks
@@ -152,16 +156,18 @@ __global__ __launch_bounds__(kThreads) void absorb_bf16_kernel(const uint16_t* _
 // n_abs is a multiple of 8, so the absorb blocks keep their XCD placement.
 template <bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) void absorb_rope_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ wuk, void* __restrict__ out,
-    int n_tok, int H, int n_abs, const uint16_t* q_rope, uint16_t* q_rot,
-    const int32_t* pos, double base, const double* freq) {
+    const uint16_t* __restrict__ q, long q_rs, const uint16_t* __restrict__ wuk,
+    void* __restrict__ out, long o_rs, int n_tok, int H, int n_abs, const uint16_t* q_rope,
+    VecStrides si, uint16_t* q_rot, VecStrides so, const int32_t* pos, double base,
+    const double* freq) {
   __shared__ __attribute__((aligned(16))) char smem[kAbsorbLds];   // either half's LDS
   const int bid = blockIdx.x;
   if (bid < n_abs) {
-    absorb_bf16_block<OUT_BF16>(bid, (lds_char*)smem, q, wuk, out, n_tok, H);
+    absorb_bf16_block<OUT_BF16>(bid, (lds_char*)smem, q, q_rs, wuk, out, o_rs, n_tok, H);
   } else {
     const int r = bid - n_abs, n_hb = (H + kRope64Heads - 1) / kRope64Heads;
-    rope64_block<true>(r / n_hb, r % n_hb, (lds_char*)smem, q_rope, q_rot, pos, H, base, freq);
+    rope64_block<true>(r / n_hb, r % n_hb, (lds_char*)smem, q_rope, si, q_rot, so, pos, H, base,
+                       freq);
   }
 }
 
@@ -172,13 +178,13 @@ constexpr int kF32Dims = 256;
 
 // part: kThreads / 64 x kF32Dims floats of LDS for the partial sums
 __device__ __forceinline__ void absorb_f32_block(int nh, int y, float* part,
-                                                 const float* __restrict__ q,
+                                                 const float* __restrict__ q, long q_rs,
                                                  const float* __restrict__ wuk,
-                                                 float* __restrict__ out, int H) {
+                                                 float* __restrict__ out, long o_rs, int H) {
   const int h = nh % H;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int d0 = y * kF32Dims;
-  const float* qr = q + (size_t)nh * kDh + 32 * w;
+  const float* qr = q + (size_t)nh * q_rs + 32 * w;
   const float* wh = wuk + ((size_t)h * kDh + 32 * w) * kDc + d0;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
@@ -191,70 +197,74 @@ __device__ __forceinline__ void absorb_f32_block(int nh, int y, float* part,
   for (int i = 0; i < 4; ++i) part[w * kF32Dims + lane + 64 * i] = acc[i];
   __syncthreads();
   const int d = threadIdx.x;
-  out[(size_t)nh * kDc + d0 + d] =
+  out[(size_t)nh * o_rs + d0 + d] =
       ((part[d] + part[kF32Dims + d]) + part[2 * kF32Dims + d]) + part[3 * kF32Dims + d];
 }
 
 __global__ __launch_bounds__(kThreads) void absorb_f32_kernel(const float* __restrict__ q,
+                                                              long q_rs,
                                                               const float* __restrict__ wuk,
-                                                              float* __restrict__ out, int n_tok,
+                                                              float* __restrict__ out, long o_rs,
                                                               int H) {
   __shared__ float part[kThreads / 64 * kF32Dims];
-  absorb_f32_block(blockIdx.x, blockIdx.y, part, q, wuk, out, H);
+  absorb_f32_block(blockIdx.x, blockIdx.y, part, q, q_rs, wuk, out, o_rs, H);
 }
 
 // fp32 query side in one launch: block 2*(n*H + h) + y absorbs as
 // absorb_f32_kernel's block (n*H + h, y) does, the rest rotate as the fp32
 // d_r = 64 rope kernel does; the two halves touch disjoint buffers.
 __global__ __launch_bounds__(kThreads) void absorb_rope_f32_kernel(
-    const float* __restrict__ q, const float* __restrict__ wuk, float* __restrict__ out, int H,
-    int n_abs, const float* q_rope, float* q_rot, const int32_t* pos, double base,
-    const double* freq) {
+    const float* __restrict__ q, long q_rs, const float* __restrict__ wuk,
+    float* __restrict__ out, long o_rs, int H, int n_abs, const float* q_rope, VecStrides si,
+    float* q_rot, VecStrides so, const int32_t* pos, double base, const double* freq) {
   __shared__ __attribute__((aligned(16))) float part[kThreads / 64 * kF32Dims];   // either half's LDS
   const int bid = blockIdx.x;
   if (bid < n_abs) {
-    absorb_f32_block(bid >> 1, bid & 1, part, q, wuk, out, H);
+    absorb_f32_block(bid >> 1, bid & 1, part, q, q_rs, wuk, out, o_rs, H);
   } else {
     const int r = bid - n_abs, n_hb = (H + kRope64Heads - 1) / kRope64Heads;
-    rope64_block<false>(r / n_hb, r % n_hb, (lds_char*)part, q_rope, q_rot, pos, H, base, freq);
+    rope64_block<false>(r / n_hb, r % n_hb, (lds_char*)part, q_rope, si, q_rot, so, pos, H, base,
+                        freq);
   }
 }
 
 }  // namespace
 
-hipError_t launch_absorb(const void* q_nope, const void* w_uk, void* q_lat, int in_bf16,
-                         int out_bf16, int n_tok, int H, hipStream_t s) {
+hipError_t launch_absorb(const void* q_nope, long q_rs, const void* w_uk, void* q_lat, long o_rs,
+                         int in_bf16, int out_bf16, int n_tok, int H, hipStream_t s) {
   if (n_tok == 0) return hipSuccess;
   if (in_bf16) {
     const dim3 grid(kNumXcd * ((H + kNumXcd - 1) / kNumXcd) * 4);
     if (out_bf16)
       hipLaunchKernelGGL(absorb_bf16_kernel<true>, grid, dim3(kThreads), 0, s,
-                         (const uint16_t*)q_nope, (const uint16_t*)w_uk, q_lat, n_tok, H);
+                         (const uint16_t*)q_nope, q_rs, (const uint16_t*)w_uk, q_lat, o_rs, n_tok,
+                         H);
     else
       hipLaunchKernelGGL(absorb_bf16_kernel<false>, grid, dim3(kThreads), 0, s,
-                         (const uint16_t*)q_nope, (const uint16_t*)w_uk, q_lat, n_tok, H);
+                         (const uint16_t*)q_nope, q_rs, (const uint16_t*)w_uk, q_lat, o_rs, n_tok,
+                         H);
   } else {
     hipLaunchKernelGGL(absorb_f32_kernel, dim3(n_tok * H, kDc / kF32Dims), dim3(kThreads), 0, s,
-                       (const float*)q_nope, (const float*)w_uk, (float*)q_lat, n_tok, H);
+                       (const float*)q_nope, q_rs, (const float*)w_uk, (float*)q_lat, o_rs, H);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_absorb_rope(const uint16_t* q_nope, const uint16_t* w_uk, void* q_lat,
-                              int out_bf16, const uint16_t* q_rope, uint16_t* q_rot,
-                              const int32_t* pos, int n_tok, int H, double base,
-                              const double* freq, hipStream_t s) {
+hipError_t launch_absorb_rope(const uint16_t* q_nope, long q_rs, const uint16_t* w_uk,
+                              void* q_lat, long o_rs, int out_bf16, const uint16_t* q_rope,
+                              VecStrides si, uint16_t* q_rot, VecStrides so, const int32_t* pos,
+                              int n_tok, int H, double base, const double* freq, hipStream_t s) {
   if (n_tok == 0) return hipSuccess;
   const int n_abs = kNumXcd * ((H + kNumXcd - 1) / kNumXcd) * 4;
   const int n_rope = n_tok * ((H + kRope64Heads - 1) / kRope64Heads);
   static_assert(kRope64Threads == kThreads, "one block size for both halves");
   const dim3 grid(n_abs + n_rope);
   if (out_bf16)
-    hipLaunchKernelGGL(absorb_rope_kernel<true>, grid, dim3(kThreads), 0, s, q_nope, w_uk, q_lat,
-                       n_tok, H, n_abs, q_rope, q_rot, pos, base, freq);
+    hipLaunchKernelGGL(absorb_rope_kernel<true>, grid, dim3(kThreads), 0, s, q_nope, q_rs, w_uk,
+                       q_lat, o_rs, n_tok, H, n_abs, q_rope, si, q_rot, so, pos, base, freq);
   else
-    hipLaunchKernelGGL(absorb_rope_kernel<false>, grid, dim3(kThreads), 0, s, q_nope, w_uk, q_lat,
-                       n_tok, H, n_abs, q_rope, q_rot, pos, base, freq);
+    hipLaunchKernelGGL(absorb_rope_kernel<false>, grid, dim3(kThreads), 0, s, q_nope, q_rs, w_uk,
+                       q_lat, o_rs, n_tok, H, n_abs, q_rope, si, q_rot, so, pos, base, freq);
   return hipGetLastError();
 }
 
@@ -262,16 +272,17 @@ hipError_t launch_absorb_rope(const uint16_t* q_nope, const uint16_t* w_uk, void
 
 namespace mla {
 
-hipError_t launch_absorb_rope_f32(const float* q_nope, const float* w_uk, float* q_lat,
-                                  const float* q_rope, float* q_rot, const int32_t* pos, int n_tok,
-                                  int H, double base, const double* freq, hipStream_t s) {
+hipError_t launch_absorb_rope_f32(const float* q_nope, long q_rs, const float* w_uk, float* q_lat,
+                                  long o_rs, const float* q_rope, VecStrides si, float* q_rot,
+                                  VecStrides so, const int32_t* pos, int n_tok, int H,
+                                  double base, const double* freq, hipStream_t s) {
   if (n_tok == 0) return hipSuccess;
   static_assert(kRope64Threads == kThreads, "one block size for both halves");
   static_assert(kThreads / 64 * kF32Dims * 4 >= 512, "the rope (cos, sin) table fits");
   const int n_abs = n_tok * H * (kDc / kF32Dims);
   const int n_rope = n_tok * ((H + kRope64Heads - 1) / kRope64Heads);
   hipLaunchKernelGGL(absorb_rope_f32_kernel, dim3(n_abs + n_rope), dim3(kThreads), 0, s, q_nope,
-                     w_uk, q_lat, H, n_abs, q_rope, q_rot, pos, base, freq);
+                     q_rs, w_uk, q_lat, o_rs, H, n_abs, q_rope, si, q_rot, so, pos, base, freq);
   return hipGetLastError();
 }
 

@@ -238,8 +238,9 @@ void decode_mfma_kernel(DecodeParams p) {
 #pragma unroll
       for (int ht = 0; ht < 2; ++ht) {
         const int r = row0 + 32 * hh + 16 * ht + i16;
-        const uint16_t* ql = (const uint16_t*)p.q_lat + ((size_t)b * p.R + r) * kDc + 8 * G4;
-        const uint16_t* qr = (const uint16_t*)p.q_rope + ((size_t)b * p.R + r) * kDr + 8 * G4;
+        const size_t qrow = (size_t)b * p.R + r;
+        const uint16_t* ql = (const uint16_t*)p.q_lat + qrow * p.q_lat_stride + 8 * G4;
+        const uint16_t* qr = (const uint16_t*)p.q_rope + qrow * p.q_rope_stride + 8 * G4;
 #pragma unroll
         for (int kk = 0; kk < 9; ++kk) {
           const int ks = k0 + kk;

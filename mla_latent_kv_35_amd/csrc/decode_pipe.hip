@@ -215,8 +215,8 @@ void decode_pipe_kernel(DecodeParams p) {
   {
     const bool live = my_row < p.R;
     const size_t qrow = (size_t)b * p.R + (live ? my_row : 0);
-    const uint16_t* ql = (const uint16_t*)p.q_lat + qrow * kDc + 8 * h;
-    const uint16_t* qr = (const uint16_t*)p.q_rope + qrow * kDr + 8 * h;
+    const uint16_t* ql = (const uint16_t*)p.q_lat + qrow * p.q_lat_stride + 8 * h;
+    const uint16_t* qr = (const uint16_t*)p.q_rope + qrow * p.q_rope_stride + 8 * h;
 #pragma clang loop unroll(full)
     for (int ks = 0; ks < 36; ++ks) {
       const bf16x8_t v = load_bf16x8(ks >= 32 ? qr + 16 * (ks - 32) : ql + 16 * ks);

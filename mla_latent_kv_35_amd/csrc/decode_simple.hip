@@ -58,9 +58,10 @@ __global__ __launch_bounds__(kThreads) void decode_simple_f32_kernel(DecodeParam
 #pragma unroll
   for (int i = 0; i < 8; ++i) u[i] = 0.f;
   if (!bad) {
-    const float* qrow = (const float*)p.q_lat + ((size_t)b * p.R + r) * kDc + 8 * lane;
+    const size_t qi = (size_t)b * p.R + r;   // query row
+    const float* qrow = (const float*)p.q_lat + qi * p.q_lat_stride + 8 * lane;
     const f32x4_t q0 = *(const f32x4_t*)qrow, q1 = *(const f32x4_t*)(qrow + 4);
-    const float qr = ((const float*)p.q_rope)[((size_t)b * p.R + r) * kDr + lane];
+    const float qr = ((const float*)p.q_rope)[qi * p.q_rope_stride + lane];
     const float* ckv = (const float*)p.ckv;
     const float* kr = (const float*)p.kr;
     for (int c0 = tok0 + kBatch * w; c0 < lim; c0 += kBatch * kWaves) {

@@ -18,12 +18,60 @@ constexpr size_t kWsAlign = 256;
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 bool is_float_dt(int dt) { return dt == MLA_F32 || dt == MLA_BF16; }
+int elt_bytes(int dt) { return dt == MLA_F32 ? 4 : dt == MLA_BF16 ? 2 : 1; }
+
+// Strides beyond this many elements are rejected (offsets stay far inside 64 bits).
+constexpr int64_t kMaxStride = int64_t(1) << 40;
+
+// Row stride of rows `len` elements long whose starts must stay 16-byte
+// aligned: 0 selects len; negative, shorter than a row or huge is a shape
+// error, a misaligned one unsupported.
+int row_stride(int64_t given, int len, int dt, long* out) {
+  if (given < 0 || given > kMaxStride) return MLA_ERR_SHAPE;
+  const int64_t r = given == 0 ? len : given;
+  if (r < len) return MLA_ERR_SHAPE;
+  if ((r * elt_bytes(dt)) % 16 != 0) return MLA_ERR_UNSUPPORTED;
+  *out = (long)r;
+  return MLA_OK;
+}
+
+// Token and head strides of rope vectors (0 selects the packed ones);
+// out_vecs: the vectors are written, so they must not overlap one another
+// (checked for the nested orders: heads inside tokens or tokens inside heads).
+int vec_strides(int64_t tok, int64_t head, int n_tok, int n_heads, int d, bool out_vecs,
+                VecStrides* st) {
+  if (tok < 0 || head < 0 || tok > kMaxStride || head > kMaxStride) return MLA_ERR_SHAPE;
+  st->tok = (long)(tok == 0 ? (int64_t)n_heads * d : tok);
+  st->head = (long)(head == 0 ? d : head);
+  if (out_vecs) {
+    const int64_t t = n_tok > 1 ? st->tok : INT64_MAX, h = n_heads > 1 ? st->head : INT64_MAX;
+    const bool heads_inner = h >= d && (n_tok == 1 || t >= (int64_t)(n_heads - 1) * h + d);
+    const bool tokens_inner = t >= d && (n_heads == 1 || h >= (int64_t)(n_tok - 1) * t + d);
+    if (!heads_inner && !tokens_inner) return MLA_ERR_SHAPE;
+  }
+  return MLA_OK;
+}
+
+// Rope input and output strides; the same memory must come with the same strides.
+int rope_strides(const void* x_in, const void* x_out, int n_tok, int n_heads, int d_r,
+                 int64_t in_tok, int64_t in_head, int64_t out_tok, int64_t out_head,
+                 VecStrides* si, VecStrides* so) {
+  int st = vec_strides(in_tok, in_head, n_tok, n_heads, d_r, false, si);
+  if (st != MLA_OK) return st;
+  st = vec_strides(out_tok, out_head, n_tok, n_heads, d_r, true, so);
+  if (st != MLA_OK) return st;
+  if (x_in == x_out && x_in && (si->tok != so->tok || si->head != so->head)) return MLA_ERR_SHAPE;
+  return MLA_OK;
+}
+
+// Query rows per workgroup of the decode kernel for this latent pool dtype.
+int kernel_rows(int ckv_dt) { return ckv_dt == MLA_BF16 ? 128 : ckv_dt == MLA_FP8_E4M3 ? 64 : 1; }
 
 struct Plan {
   int split_tokens = 0;
   int n_split = 1;
-  int rows = kRowsPerGroup;  // query rows per workgroup (MFMA kernels: 64 or 128)
-  int G = 1;              // row groups per sequence (MFMA kernels)
+  int rows = 1;           // query rows per workgroup (kernel_rows)
+  int G = 1;              // row groups per sequence
   size_t part_u_bytes = 0;
   size_t ws_bytes = 0;
 };
@@ -31,7 +79,6 @@ struct Plan {
 // Checks everything that does not need a device pointer.
 int check_shape(const mla_decode_args* a) {
   if (!a) return MLA_ERR_NULL;
-  if (a->reserved0 != 0) return MLA_ERR_SHAPE;
   if (a->B < 1 || a->H < 1 || a->T < 1) return MLA_ERR_SHAPE;
   if (a->T > 2) return MLA_ERR_UNSUPPORTED;
   if (a->d_c != kDc || a->d_r != kDr) return MLA_ERR_UNSUPPORTED;
@@ -54,6 +101,13 @@ int check_shape(const mla_decode_args* a) {
   } else {
     return MLA_ERR_DTYPE;
   }
+  if (a->heads_per_wg < 0) return MLA_ERR_SHAPE;
+  if (a->heads_per_wg != 0 && a->heads_per_wg != kernel_rows(a->ckv_dt)) return MLA_ERR_UNSUPPORTED;
+  long st;
+  int e = row_stride(a->q_lat_stride, kDc, a->q_dt, &st);
+  if (e != MLA_OK) return e;
+  e = row_stride(a->q_rope_stride, kDr, a->q_dt, &st);
+  if (e != MLA_OK) return e;
   return MLA_OK;
 }
 
@@ -68,8 +122,7 @@ Plan make_plan(const mla_decode_args* a) {
   const int64_t total = a->total_tokens > 0 ? a->total_tokens : (int64_t)a->B * Lmax;
   const int64_t pages_total = (total + kPage - 1) / kPage;
   const int64_t max_pages = (Lmax + kPage - 1) / kPage;
-  // bf16 pools: 128 rows per workgroup (the pipelined kernel); fp8 pools: 64
-  if (a->ckv_dt == MLA_BF16) pl.rows = 128;
+  pl.rows = kernel_rows(a->ckv_dt);
   pl.G = (int)((R + pl.rows - 1) / pl.rows);
   if (a->split_tokens > 0) {
     pl.split_tokens = a->split_tokens;
@@ -79,7 +132,7 @@ Plan make_plan(const mla_decode_args* a) {
     int64_t sp = (max_pages + want - 1) / want;
     pl.split_tokens = (int)(std::max<int64_t>(sp, 1) * kPage);
   } else {
-    // MFMA kernel: units of (sequence, split, 64-row group). Uniform batches
+    // MFMA kernels: units of (sequence, split, row group). Uniform batches
     // get one unit per CU; ragged ones four per CU so the uneven tails balance.
     const bool ragged = total * 10 < (int64_t)a->B * Lmax * 9;
     const int64_t target = ragged ? 4 * kNumCu : kNumCu;
@@ -156,75 +209,113 @@ const char* mla_status_str(int status) {
 
 int mla_abi_version(void) { return MLA_ABI_VERSION; }
 
-int mla_absorb_q(const void* q_nope, const void* w_uk, void* q_lat, int q_dt, int out_dt,
-                 int n_tok, int H, int d_h, int d_c, void* stream) {
+namespace {
+// Host checks shared by mla_absorb_q and mla_absorb_q_rope.
+int check_absorb(int q_dt, int out_dt, int n_tok, int H, int d_h, int d_c, int64_t q_row_stride,
+                 int64_t out_row_stride, long* q_rs, long* o_rs) {
   if (n_tok < 0 || H < 1) return MLA_ERR_SHAPE;
   if (d_h != kDh || d_c != kDc) return MLA_ERR_UNSUPPORTED;
   if (!is_float_dt(q_dt) || !is_float_dt(out_dt)) return MLA_ERR_DTYPE;
   if (q_dt == MLA_F32 && out_dt != MLA_F32) return MLA_ERR_DTYPE;
+  const int e = row_stride(q_row_stride, kDh, q_dt, q_rs);
+  return e != MLA_OK ? e : row_stride(out_row_stride, kDc, out_dt, o_rs);
+}
+}  // namespace
+
+int mla_absorb_q(const void* q_nope, const void* w_uk, void* q_lat, int q_dt, int out_dt,
+                 int n_tok, int H, int d_h, int d_c, int64_t q_row_stride,
+                 int64_t out_row_stride, void* stream) {
+  long q_rs, o_rs;
+  const int st = check_absorb(q_dt, out_dt, n_tok, H, d_h, d_c, q_row_stride, out_row_stride,
+                              &q_rs, &o_rs);
+  if (st != MLA_OK) return st;
   if (n_tok == 0) return MLA_OK;
   if (!q_nope || !w_uk || !q_lat) return MLA_ERR_NULL;
   if ((((uintptr_t)q_nope | (uintptr_t)w_uk | (uintptr_t)q_lat) & 15) != 0) return MLA_ERR_UNSUPPORTED;
-  const hipError_t e = launch_absorb(q_nope, w_uk, q_lat, q_dt == MLA_BF16, out_dt == MLA_BF16,
-                                     n_tok, H, (hipStream_t)stream);
+  const hipError_t e = launch_absorb(q_nope, q_rs, w_uk, q_lat, o_rs, q_dt == MLA_BF16,
+                                     out_dt == MLA_BF16, n_tok, H, (hipStream_t)stream);
   return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
 }
 
 int mla_rope(const void* x_in, void* x_out, int dt, const int32_t* pos, int n_tok, int n_heads,
-             int d_r, double base, void* stream) {
+             int d_r, double base, int64_t in_tok_stride, int64_t in_head_stride,
+             int64_t out_tok_stride, int64_t out_head_stride, void* stream) {
   if (n_tok < 0 || n_heads < 1) return MLA_ERR_SHAPE;
   if (d_r < 2 || d_r > 256 || d_r % 2 != 0) return MLA_ERR_UNSUPPORTED;
   if (!is_float_dt(dt)) return MLA_ERR_DTYPE;
   if (!(base > 0.0) || !isfinite(base)) return MLA_ERR_SHAPE;
+  VecStrides si, so;
+  const int st = rope_strides(x_in, x_out, n_tok, n_heads, d_r, in_tok_stride, in_head_stride,
+                              out_tok_stride, out_head_stride, &si, &so);
+  if (st != MLA_OK) return st;
   if (n_tok == 0) return MLA_OK;
   if (!x_in || !x_out || !pos) return MLA_ERR_NULL;
-  const hipError_t e = launch_rope(x_in, x_out, dt == MLA_BF16, pos, n_tok, n_heads, d_r, base,
-                                   nullptr, (hipStream_t)stream);
+  const hipError_t e = launch_rope(x_in, si, x_out, so, dt == MLA_BF16, pos, n_tok, n_heads, d_r,
+                                   base, nullptr, (hipStream_t)stream);
   return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
 }
 
 int mla_rope_freq(const void* x_in, void* x_out, int dt, const int32_t* pos, int n_tok,
-                  int n_heads, int d_r, const double* theta, void* stream) {
+                  int n_heads, int d_r, const double* theta, int64_t in_tok_stride,
+                  int64_t in_head_stride, int64_t out_tok_stride, int64_t out_head_stride,
+                  void* stream) {
   if (n_tok < 0 || n_heads < 1) return MLA_ERR_SHAPE;
   if (d_r < 2 || d_r > 256 || d_r % 2 != 0) return MLA_ERR_UNSUPPORTED;
   if (!is_float_dt(dt)) return MLA_ERR_DTYPE;
+  VecStrides si, so;
+  const int st = rope_strides(x_in, x_out, n_tok, n_heads, d_r, in_tok_stride, in_head_stride,
+                              out_tok_stride, out_head_stride, &si, &so);
+  if (st != MLA_OK) return st;
   if (n_tok == 0) return MLA_OK;
   if (!x_in || !x_out || !pos || !theta) return MLA_ERR_NULL;
-  const hipError_t e = launch_rope(x_in, x_out, dt == MLA_BF16, pos, n_tok, n_heads, d_r, 1.0,
-                                   theta, (hipStream_t)stream);
+  const hipError_t e = launch_rope(x_in, si, x_out, so, dt == MLA_BF16, pos, n_tok, n_heads, d_r,
+                                   1.0, theta, (hipStream_t)stream);
   return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
 }
 
 int mla_absorb_q_rope(const void* q_nope, const void* w_uk, void* q_lat, int q_dt, int out_dt,
                       const void* q_rope, void* q_rot, int rope_dt, const int32_t* pos,
                       int n_tok, int H, int d_h, int d_c, int d_r, double base,
-                      const double* theta, void* stream) {
-  if (n_tok < 0 || H < 1) return MLA_ERR_SHAPE;
-  if (d_h != kDh || d_c != kDc) return MLA_ERR_UNSUPPORTED;
+                      const double* theta, int64_t q_row_stride, int64_t out_row_stride,
+                      int64_t rope_row_stride, int64_t rot_row_stride, void* stream) {
+  long q_rs, o_rs;
+  int st = check_absorb(q_dt, out_dt, n_tok, H, d_h, d_c, q_row_stride, out_row_stride, &q_rs,
+                        &o_rs);
+  if (st != MLA_OK) return st;
   if (d_r < 2 || d_r > 256 || d_r % 2 != 0) return MLA_ERR_UNSUPPORTED;
-  if (!is_float_dt(q_dt) || !is_float_dt(out_dt) || !is_float_dt(rope_dt)) return MLA_ERR_DTYPE;
-  if (q_dt == MLA_F32 && out_dt != MLA_F32) return MLA_ERR_DTYPE;
+  if (!is_float_dt(rope_dt)) return MLA_ERR_DTYPE;
   if (!theta && (!(base > 0.0) || !isfinite(base))) return MLA_ERR_SHAPE;
+  // rope rows: token stride H * r, head stride r
+  if (rope_row_stride < 0 || rot_row_stride < 0 || rope_row_stride > kMaxStride ||
+      rot_row_stride > kMaxStride)
+    return MLA_ERR_SHAPE;
+  const int64_t rr = rope_row_stride ? rope_row_stride : d_r;
+  const int64_t ro = rot_row_stride ? rot_row_stride : d_r;
+  VecStrides si, so;
+  st = rope_strides(q_rope, q_rot, n_tok, H, d_r, rr * H, rr, ro * H, ro, &si, &so);
+  if (st != MLA_OK) return st;
   if (n_tok == 0) return MLA_OK;
   if (!q_nope || !w_uk || !q_lat || !q_rope || !q_rot || !pos) return MLA_ERR_NULL;
   if ((((uintptr_t)q_nope | (uintptr_t)w_uk | (uintptr_t)q_lat) & 15) != 0) return MLA_ERR_UNSUPPORTED;
   const hipStream_t s = (hipStream_t)stream;
+  // the fused kernel's rope half reads and writes 16-byte slices
+  const bool rope_vec = d_r == 64 && (((uintptr_t)q_rope | (uintptr_t)q_rot) & 15) == 0 &&
+                        ((rr | ro) * elt_bytes(rope_dt)) % 16 == 0;
   hipError_t e;
-  if (q_dt == MLA_BF16 && rope_dt == MLA_BF16 && d_r == 64 &&
-      (((uintptr_t)q_rope | (uintptr_t)q_rot) & 15) == 0) {
-    e = launch_absorb_rope((const uint16_t*)q_nope, (const uint16_t*)w_uk, q_lat,
-                           out_dt == MLA_BF16, (const uint16_t*)q_rope, (uint16_t*)q_rot, pos,
-                           n_tok, H, theta ? 1.0 : base, theta, s);
-  } else if (q_dt == MLA_F32 && rope_dt == MLA_F32 && d_r == 64 &&
-             (((uintptr_t)q_rope | (uintptr_t)q_rot) & 15) == 0) {
-    e = launch_absorb_rope_f32((const float*)q_nope, (const float*)w_uk, (float*)q_lat,
-                               (const float*)q_rope, (float*)q_rot, pos, n_tok, H,
+  if (q_dt == MLA_BF16 && rope_dt == MLA_BF16 && rope_vec) {
+    e = launch_absorb_rope((const uint16_t*)q_nope, q_rs, (const uint16_t*)w_uk, q_lat, o_rs,
+                           out_dt == MLA_BF16, (const uint16_t*)q_rope, si, (uint16_t*)q_rot, so,
+                           pos, n_tok, H, theta ? 1.0 : base, theta, s);
+  } else if (q_dt == MLA_F32 && rope_dt == MLA_F32 && rope_vec) {
+    e = launch_absorb_rope_f32((const float*)q_nope, q_rs, (const float*)w_uk, (float*)q_lat,
+                               o_rs, (const float*)q_rope, si, (float*)q_rot, so, pos, n_tok, H,
                                theta ? 1.0 : base, theta, s);
   } else {
-    e = launch_absorb(q_nope, w_uk, q_lat, q_dt == MLA_BF16, out_dt == MLA_BF16, n_tok, H, s);
+    e = launch_absorb(q_nope, q_rs, w_uk, q_lat, o_rs, q_dt == MLA_BF16, out_dt == MLA_BF16,
+                      n_tok, H, s);
     if (e == hipSuccess)
-      e = launch_rope(q_rope, q_rot, rope_dt == MLA_BF16, pos, n_tok, H, d_r, theta ? 1.0 : base,
-                      theta, s);
+      e = launch_rope(q_rope, si, q_rot, so, rope_dt == MLA_BF16, pos, n_tok, H, d_r,
+                      theta ? 1.0 : base, theta, s);
   }
   return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
 }
@@ -252,13 +343,14 @@ double mla_yarn_mscale(double factor, double coef) {
 }
 
 int mla_decode_plan(const mla_decode_args* args, int* split_tokens, int* n_split,
-                    size_t* workspace_bytes) {
+                    int* heads_per_wg, size_t* workspace_bytes) {
   const int st = check_shape(args);
   if (st != MLA_OK) return st;
   const Plan pl = make_plan(args);
   if (pl.n_split > kMaxSplits) return MLA_ERR_UNSUPPORTED;
   if (split_tokens) *split_tokens = pl.split_tokens;
   if (n_split) *n_split = pl.n_split;
+  if (heads_per_wg) *heads_per_wg = pl.rows;
   if (workspace_bytes) *workspace_bytes = pl.ws_bytes;
   return MLA_OK;
 }
@@ -314,6 +406,8 @@ int mla_decode_paged(const mla_decode_args* a, void* stream) {
   p.out_bf16 = a->out_dt == MLA_BF16;
   p.scale_log2 = a->softmax_scale * kLog2e;
   p.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
+  p.q_lat_stride = a->q_lat_stride ? (long)a->q_lat_stride : kDc;
+  p.q_rope_stride = a->q_rope_stride ? (long)a->q_rope_stride : kDr;
   const int64_t units = (int64_t)a->B * pl.n_split * pl.G;
   if (units > (int64_t)1 << 30) return MLA_ERR_UNSUPPORTED;
   p.n_units = (int)units;
@@ -390,16 +484,22 @@ int mla_stream_read(const void* src, size_t bytes, void* sink, void* stream) {
 }
 
 int mla_out_proj(const void* u, const void* w_uv, void* o, int u_dt, int w_dt, int o_dt, int n_tok,
-                 int H, int d_h, int d_c, void* stream) {
+                 int H, int d_h, int d_c, int64_t u_row_stride, int64_t o_row_stride,
+                 void* stream) {
   if (n_tok < 0 || H < 1) return MLA_ERR_SHAPE;
   if (d_h != kDh || d_c != kDc) return MLA_ERR_UNSUPPORTED;
   if (!is_float_dt(u_dt) || !is_float_dt(w_dt) || !is_float_dt(o_dt)) return MLA_ERR_DTYPE;
   if (w_dt == MLA_F32 && (u_dt != MLA_F32 || o_dt != MLA_F32)) return MLA_ERR_DTYPE;
+  long u_rs, o_rs;
+  int st = row_stride(u_row_stride, kDc, u_dt, &u_rs);
+  if (st == MLA_OK) st = row_stride(o_row_stride, kDh, o_dt, &o_rs);
+  if (st != MLA_OK) return st;
   if (n_tok == 0) return MLA_OK;
   if (!u || !w_uv || !o) return MLA_ERR_NULL;
   if ((((uintptr_t)u | (uintptr_t)w_uv | (uintptr_t)o) & 15) != 0) return MLA_ERR_UNSUPPORTED;
-  const hipError_t e = launch_out_proj(u, w_uv, o, u_dt == MLA_BF16, w_dt == MLA_BF16,
-                                       o_dt == MLA_BF16, n_tok, H, (hipStream_t)stream);
+  const hipError_t e = launch_out_proj_strided(u, (long)H * u_rs, u_rs, w_uv, o, o_rs,
+                                               u_dt == MLA_BF16, w_dt == MLA_BF16,
+                                               o_dt == MLA_BF16, n_tok, H, (hipStream_t)stream);
   return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
 }
 
@@ -423,7 +523,7 @@ int mla_expand_kv(const void* c, const void* w_uk, const void* w_uv, void* k_nop
         w_dt == MLA_BF16
             ? launch_gemm_nt(c, c_dt == MLA_BF16, (const uint16_t*)w, out, out_dt == MLA_BF16,
                              n_tok, H * kDh, kDc, s)
-            : launch_out_proj_strided(c, kDc, 0, w, out, 0, 0, 0, n_tok, H, s);
+            : launch_out_proj_strided(c, kDc, 0, w, out, kDh, 0, 0, 0, n_tok, H, s);
     if (e != hipSuccess) return MLA_ERR_LAUNCH;
   }
   return MLA_OK;

@@ -46,13 +46,15 @@ hipError_t launch_gemm_nt(const void* A, int a_bf16, const uint16_t* B, void* C,
                           int N, int K, hipStream_t s);
 // absorb (bf16 queries, bf16 W_UK) and d_r = 64 bf16 rope in one launch;
 // freq null = base^(-2i/64)
-hipError_t launch_absorb_rope(const uint16_t* q_nope, const uint16_t* w_uk, void* q_lat,
-                              int out_bf16, const uint16_t* q_rope, uint16_t* q_rot,
-                              const int32_t* pos, int n_tok, int H, double base,
-                              const double* freq, hipStream_t s);
+// (strides as launch_absorb and launch_rope; rope vectors 16-byte aligned)
+hipError_t launch_absorb_rope(const uint16_t* q_nope, long q_rs, const uint16_t* w_uk,
+                              void* q_lat, long o_rs, int out_bf16, const uint16_t* q_rope,
+                              VecStrides si, uint16_t* q_rot, VecStrides so, const int32_t* pos,
+                              int n_tok, int H, double base, const double* freq, hipStream_t s);
 // the same for fp32 queries, W_UK, q_lat and rope data
-hipError_t launch_absorb_rope_f32(const float* q_nope, const float* w_uk, float* q_lat,
-                                  const float* q_rope, float* q_rot, const int32_t* pos, int n_tok,
-                                  int H, double base, const double* freq, hipStream_t s);
+hipError_t launch_absorb_rope_f32(const float* q_nope, long q_rs, const float* w_uk, float* q_lat,
+                                  long o_rs, const float* q_rope, VecStrides si, float* q_rot,
+                                  VecStrides so, const int32_t* pos, int n_tok, int H,
+                                  double base, const double* freq, hipStream_t s);
 
 }  // namespace mla

@@ -22,8 +22,8 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 // Everything a decode kernel needs; filled by the host planner.
 struct DecodeParams {
-  const void* q_lat;        // [B][R][512]
-  const void* q_rope;       // [B][R][64]
+  const void* q_lat;        // [B][R][512], row stride q_lat_stride elements
+  const void* q_rope;       // [B][R][64], row stride q_rope_stride elements
   const void* ckv;          // [n_pages][64][512]
   const void* kr;           // [n_pages][64][64]
   const float* ckv_scale;   // [n_pages][64] (fp8 only)
@@ -43,6 +43,8 @@ struct DecodeParams {
   int per_xcd;              // grid = per_xcd * 8 (XCD-major unit numbering)
   float scale_log2;         // softmax_scale * log2(e)
   int spin_limit;           // polls of a bounded wait before it gives up (fp8 kernel)
+  long q_lat_stride;        // elements between consecutive query rows of q_lat
+  long q_rope_stride;       // ... and of q_rope
 };
 
 struct CombineParams {
@@ -68,22 +70,31 @@ struct CombineParams {
 
 hipError_t launch_decode_mfma_fp8(const DecodeParams& p, hipStream_t s);
 hipError_t launch_decode_simple_f32(const DecodeParams& p, hipStream_t s);
-// fp8: E4M3FN latent pool with per-token scales; rows: query rows per workgroup (64 or 128)
+// bf16 latent and rope pools, 128 query rows per workgroup
 hipError_t launch_decode_pipe(const DecodeParams& p, hipStream_t s);
 hipError_t launch_stream_read(const void* src, size_t bytes, void* sink, hipStream_t s);
 hipError_t launch_combine(const CombineParams& p, hipStream_t s);
 // combine fused with the value up-projection; needs p.w_uv, p.o, n_split <= 64
 hipError_t launch_combine_out(const CombineParams& p, hipStream_t s);
 
+// Element strides of the (token, head) vectors of a [n_tok][heads][d] tensor:
+// vector (n, h) starts at n * tok + h * head.
+struct VecStrides {
+  long tok, head;
+};
+
 // theta: device fp64 [d_r/2] per-pair frequencies, or null for base^(-2i/d_r)
-hipError_t launch_rope(const void* x_in, void* x_out, int bf16, const int32_t* pos, int n_tok,
-                       int n_heads, int d_r, double base, const double* theta, hipStream_t s);
-hipError_t launch_absorb(const void* q_nope, const void* w_uk, void* q_lat, int in_bf16,
-                         int out_bf16, int n_tok, int H, hipStream_t s);
-// o[n][h][:] = W[h] u(n, h), u(n, h) at n * u_tok + h * u_head elements
+hipError_t launch_rope(const void* x_in, VecStrides si, void* x_out, VecStrides so, int bf16,
+                       const int32_t* pos, int n_tok, int n_heads, int d_r, double base,
+                       const double* theta, hipStream_t s);
+// q_rs, o_rs: row strides (elements between (token, head) rows) of q_nope, q_lat
+hipError_t launch_absorb(const void* q_nope, long q_rs, const void* w_uk, void* q_lat, long o_rs,
+                         int in_bf16, int out_bf16, int n_tok, int H, hipStream_t s);
+// o[n][h][:] = W[h] u(n, h), u(n, h) at n * u_tok + h * u_head elements, o's
+// (n, h) row at (n * H + h) * o_rs
 hipError_t launch_out_proj_strided(const void* u, long u_tok, long u_head, const void* w_uv,
-                                   void* o, int u_bf16, int w_bf16, int o_bf16, int n_tok, int H,
-                                   hipStream_t s);
+                                   void* o, long o_rs, int u_bf16, int w_bf16, int o_bf16,
+                                   int n_tok, int H, hipStream_t s);
 hipError_t launch_out_proj(const void* u, const void* w_uv, void* o, int u_bf16, int w_bf16,
                            int o_bf16, int n_tok, int H, hipStream_t s);
 

@@ -39,13 +39,13 @@ constexpr int kUStage = kTokTile * kDc * 2;   // 64 KB
 
 // u row of (token n, head h) starts at n * u_tok + h * u_head elements:
 // (H * 512, 512) for per-head aggregates; (512, 0) for a latent shared by
-// every head.
+// every head. o row (n, h) starts at (n * H + h) * o_rs elements.
 template <bool U_BF16, bool O_BF16, int NJ, int TT>
 __global__ __launch_bounds__(kThreads) void out_proj_bf16_kernel(const void* __restrict__ u,
                                                                  const uint16_t* __restrict__ wuv,
-                                                                 void* __restrict__ o, int n_tok,
-                                                                 int H, int n_tb, long u_tok,
-                                                                 long u_head) {
+                                                                 void* __restrict__ o, long o_rs,
+                                                                 int n_tok, int H, int n_tb,
+                                                                 long u_tok, long u_head) {
   constexpr int JB = 2 / NJ;                          // 16-wide output blocks per wave
   __shared__ __attribute__((aligned(16))) char ush_raw[kUStage];
   lds_char* const ush = (lds_char*)ush_raw;
@@ -116,7 +116,7 @@ __global__ __launch_bounds__(kThreads) void out_proj_bf16_kernel(const void* __r
       for (int i = 0; i < 4; ++i) {
         const int n = n0 + 16 * tt + 4 * G4 + i;
         if (n < n_tok) {
-          const size_t off = ((size_t)n * H + h) * kDh + j0 + 16 * jb + i16;
+          const size_t off = ((size_t)n * H + h) * o_rs + j0 + 16 * jb + i16;
           if (O_BF16) ((uint16_t*)o)[off] = f2bf(acc[tt][jb][i]);
           else ((float*)o)[off] = acc[tt][jb][i];
         }
@@ -133,8 +133,9 @@ constexpr int kF32Blocks = kDh / (kF32Waves * kF32Rows);     // workgroups per (
 
 __global__ __launch_bounds__(64 * kF32Waves) void out_proj_f32_kernel(const float* __restrict__ u,
                                                                     const float* __restrict__ wuv,
-                                                                    float* __restrict__ o, int H,
-                                                                    long u_tok, long u_head) {
+                                                                    float* __restrict__ o,
+                                                                    long o_rs, int H, long u_tok,
+                                                                    long u_head) {
   const int nh = blockIdx.x;
   const int h = nh % H;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -157,7 +158,7 @@ __global__ __launch_bounds__(64 * kF32Waves) void out_proj_f32_kernel(const floa
     for (int i = 0; i < 4; ++i) acc = fmaf(wb[jj][i], u1[i], acc);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-    if (lane == 0) o[(size_t)nh * kDh + j0 + jj] = acc;
+    if (lane == 0) o[(size_t)nh * o_rs + j0 + jj] = acc;
   }
 }
 
@@ -165,13 +166,13 @@ __global__ __launch_bounds__(64 * kF32Waves) void out_proj_f32_kernel(const floa
 
 hipError_t launch_out_proj(const void* u, const void* w_uv, void* o, int u_bf16, int w_bf16,
                            int o_bf16, int n_tok, int H, hipStream_t s) {
-  return launch_out_proj_strided(u, (long)H * kDc, kDc, w_uv, o, u_bf16, w_bf16, o_bf16, n_tok, H,
-                                 s);
+  return launch_out_proj_strided(u, (long)H * kDc, kDc, w_uv, o, kDh, u_bf16, w_bf16, o_bf16,
+                                 n_tok, H, s);
 }
 
 hipError_t launch_out_proj_strided(const void* u, long u_tok, long u_head, const void* w_uv,
-                                   void* o, int u_bf16, int w_bf16, int o_bf16, int n_tok, int H,
-                                   hipStream_t s) {
+                                   void* o, long o_rs, int u_bf16, int w_bf16, int o_bf16,
+                                   int n_tok, int H, hipStream_t s) {
   if (n_tok == 0) return hipSuccess;
   if (w_bf16) {
     const int n_tb = (n_tok + kTokTile - 1) / kTokTile;
@@ -185,13 +186,13 @@ hipError_t launch_out_proj_strided(const void* u, long u_tok, long u_head, const
 #define MLA_OUTP_T(UB, OB, NJ)                                                                \
   if (tt == 1)                                                                                \
     hipLaunchKernelGGL((out_proj_bf16_kernel<UB, OB, NJ, 1>), grid, dim3(kThreads), 0, s, u, w, \
-                       o, n_tok, H, n_tb, u_tok, u_head);                                     \
+                       o, o_rs, n_tok, H, n_tb, u_tok, u_head);                                     \
   else if (tt == 2)                                                                           \
     hipLaunchKernelGGL((out_proj_bf16_kernel<UB, OB, NJ, 2>), grid, dim3(kThreads), 0, s, u, w, \
-                       o, n_tok, H, n_tb, u_tok, u_head);                                     \
+                       o, o_rs, n_tok, H, n_tb, u_tok, u_head);                                     \
   else                                                                                        \
     hipLaunchKernelGGL((out_proj_bf16_kernel<UB, OB, NJ, 4>), grid, dim3(kThreads), 0, s, u, w, \
-                       o, n_tok, H, n_tb, u_tok, u_head);
+                       o, o_rs, n_tok, H, n_tb, u_tok, u_head);
 #define MLA_OUTP(UB, OB)  \
   if (split_j) {          \
     MLA_OUTP_T(UB, OB, 2) \
@@ -211,7 +212,7 @@ hipError_t launch_out_proj_strided(const void* u, long u_tok, long u_head, const
 #undef MLA_OUTP_T
   } else {
     hipLaunchKernelGGL(out_proj_f32_kernel, dim3(n_tok * H, kF32Blocks), dim3(64 * kF32Waves), 0, s,
-                       (const float*)u, (const float*)w_uv, (float*)o, H, u_tok, u_head);
+                       (const float*)u, (const float*)w_uv, (float*)o, o_rs, H, u_tok, u_head);
   }
   return hipGetLastError();
 }

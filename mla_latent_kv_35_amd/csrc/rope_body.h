@@ -6,6 +6,7 @@
 #pragma once
 
 #include "mla_device.h"
+#include "mla_internal.h"
 
 namespace mla {
 
@@ -15,30 +16,35 @@ constexpr int kRope64Heads = 32;
 // d_r = 64: one workgroup per (token, 32 heads). Lanes 0..31 build the 32
 // (cos, sin) pairs of the token's position in fp64 while every thread's
 // 16-byte slice of the 32 rows is already in flight; each thread then
-// rotates its 4 (bf16) or 2 x 2 (fp32) pairs. In place is allowed: a thread
-// reads and writes only its own slice.
+// rotates its 4 (bf16) or 2 x 2 (fp32) pairs. In place (same memory, same
+// strides) is allowed: a thread reads and writes only its own slice. Vector
+// (n, h) of x_in starts at n * si.tok + h * si.head elements, of x_out at
+// n * so.tok + h * so.head; each start is 16-byte aligned.
 
 // cs_lds: 512 bytes of LDS for the token's (cos, sin) table
 template <bool BF16>
 __device__ __forceinline__ void rope64_block(int n, int hblk, lds_char* cs_lds, const void* x_in,
-                                             void* x_out, const int32_t* pos, int n_heads,
-                                             double base, const double* freq) {
+                                             VecStrides si, void* x_out, VecStrides so,
+                                             const int32_t* pos, int n_heads, double base,
+                                             const double* freq) {
   MLA_LDS double(*cs)[2] = (MLA_LDS double(*)[2])cs_lds;
   const int h0 = hblk * kRope64Heads;
   const int tid = threadIdx.x;
   // each 64-element row is 8 (bf16) or 16 (fp32) slices of 16 bytes
   constexpr int kSlices = BF16 ? 8 : 16;
   constexpr int kPerThread = kRope64Heads * kSlices / kRope64Threads;   // 1 or 2
+  constexpr int kElt = BF16 ? 2 : 4;
   u32x4_t v[kPerThread];
-  size_t off[kPerThread];
+  size_t off[kPerThread];   // byte offset of this thread's slice in x_out
   bool ok[kPerThread];
 #pragma unroll
   for (int q = 0; q < kPerThread; ++q) {
     const int e = tid + q * kRope64Threads;
     const int h = h0 + e / kSlices, c = e % kSlices;
     ok[q] = h < n_heads;
-    off[q] = (((size_t)n * n_heads + h) * 64) * (BF16 ? 2 : 4) + (size_t)c * 16;
-    if (ok[q]) v[q] = *(const u32x4_t*)((const char*)x_in + off[q]);
+    const size_t in = ((size_t)n * si.tok + (size_t)h * si.head) * kElt + (size_t)c * 16;
+    off[q] = ((size_t)n * so.tok + (size_t)h * so.head) * kElt + (size_t)c * 16;
+    if (ok[q]) v[q] = *(const u32x4_t*)((const char*)x_in + in);
   }
   if (tid < 32) {
     const double theta = freq ? freq[tid] : pow(base, -2.0 * (double)tid / 64.0);

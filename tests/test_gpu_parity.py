@@ -450,3 +450,87 @@ def test_fp8_partner_wait_gives_up_loudly(mla):
         torch.cuda.synchronize()
         ref = O.decode_step(inp)
         assert row_rel(host(u2), np.stack([ref[b]["u"][0] for b in ref])) <= TOL["fp8"]
+
+
+# --------------------------------------------------------------------------
+# Strided rows: queries as slices of one projection output
+# --------------------------------------------------------------------------
+
+def _padded(width, x_parts, dtype):
+    """[n, H, width] device tensor, NaN everywhere, with x_parts written at
+    their column offsets; returns the tensor and the column views."""
+    n, H = x_parts[0][1].shape[:2]
+    big = torch.full((n, H, width), float("nan"), dtype=dtype, device="cuda")
+    views = []
+    for off, x in x_parts:
+        big[:, :, off:off + x.shape[2]] = x
+        views.append(big[:, :, off:off + x.shape[2]])
+    return big, views
+
+
+@pytest.mark.parametrize("ckv_dt", ["bf16", "fp8", "f32"])
+@pytest.mark.parametrize("fused", [True, False])
+def test_query_slices_of_one_projection(mla, ckv_dt, fused):
+    """q_nope and q_rope as the two column slices of one [B*T][H][192 + 8]
+    tensor (a query up-projection's output; the 8 trailing columns are NaN),
+    absorbed and rotated straight from the slices into the two slices of one
+    [B*T][H][576 + 8] query tensor that the decode reads in place; u then
+    projected from a slice of a wider buffer into one. Every result equals
+    the packed path's bit for bit and matches the oracle."""
+    kw = dict(q_dt="f32", kr_dt="f32") if ckv_dt == "f32" else {}
+    cfg = synth.small_config(B=3, H=32, T=2, seq_len=300, ragged=True, permuted=True,
+                             ckv_dt=ckv_dt, seed=97, **kw)
+    inp = synth.make_inputs(cfg)
+    d = mla.upload(inp)
+    packed = mla.decode_step(d, split_tokens=64, fused=fused)
+    qdt = d.q_nope.dtype
+    _, (qn, qr) = _padded(200, [(0, d.q_nope), (128, d.q_rope)], qdt)
+    q_all = torch.full(qn.shape[:2] + (584,), float("nan"), dtype=qdt, device="cuda")
+    q_lat, q_rot = q_all[:, :, :512], q_all[:, :, 512:576]
+    if fused:
+        mla.absorb_q_rope(qn, d.w_uk, qr, d.positions, q_lat=q_lat, q_rot=q_rot)
+    else:
+        mla.absorb_q(qn, d.w_uk, out=q_lat)
+        mla.rope(qr, d.positions, out=q_rot)
+    u, lse = mla.decode_paged(q_lat, q_rot, d.cache, d.T, d.softmax_scale, split_tokens=64,
+                              out_dtype=packed["u"].dtype)
+    _, (us,) = _padded(520, [(8, u)], u.dtype)
+    o_all = torch.full(u.shape[:2] + (136,), float("nan"), dtype=u.dtype, device="cuda")
+    mla.out_proj(us, d.w_uv, out=o_all[:, :, :128])
+    torch.cuda.synchronize()
+    for name, got in (("q_lat", q_lat), ("q_rot", q_rot), ("u", u), ("lse", lse),
+                      ("o", o_all[:, :, :128])):
+        want = packed[name]
+        assert got.dtype == want.dtype and got.shape == want.shape, name
+        assert torch.equal(got.contiguous().view(torch.uint8), want.contiguous().view(torch.uint8)), name
+    # the padding columns were never written
+    assert torch.isnan(q_all[:, :, 576:].float()).all() and torch.isnan(o_all[:, :, 128:].float()).all()
+    ref = O.decode_step(inp)
+    T = cfg.T
+    for name, got in (("u", u), ("o", o_all[:, :, :128])):
+        g = host(got.contiguous())
+        gg = np.stack([g[b * T:(b + 1) * T] for b in ref])
+        assert row_rel(gg, np.stack([ref[b][name] for b in ref])) <= TOL[ckv_dt], name
+
+
+def test_rope_token_and_head_strides(mla):
+    """mla_rope over token and head strides that are not the packed ones: a
+    head-major [H][n][64] input (tokens inside heads) written into every
+    other 64-column block of a token-major output; equals the packed result
+    bit for bit, on the vectorised (aligned) and the generic (odd stride)
+    kernel alike."""
+    rng = np.random.default_rng(5)
+    n, H = 37, 12
+    x = torch.from_numpy(rng.standard_normal((n, H, 64)).astype(np.float32)).cuda().to(torch.bfloat16)
+    pos = torch.from_numpy(rng.integers(0, 1 << 17, n).astype(np.int32)).cuda()
+    want = mla.rope(x, pos)
+    xh = x.transpose(0, 1).contiguous().transpose(0, 1)            # strides (64, n * 64, 1)
+    y = torch.full((n, H, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    got = mla.rope(xh, pos, out=y[:, :, 32:96])                     # out strides (H * 128, 128, 1)
+    xo = torch.full((n, H, 67), float("nan"), dtype=torch.bfloat16, device="cuda")
+    xo[:, :, 3:] = x
+    got_odd = mla.rope(xo[:, :, 3:], pos)                           # 6-byte offset: generic kernel
+    torch.cuda.synchronize()
+    for g in (got, got_odd):
+        assert torch.equal(g.contiguous().view(torch.int16), want.view(torch.int16))
+    assert torch.isnan(y[:, :, :32].float()).all() and torch.isnan(y[:, :, 96:].float()).all()
