@@ -29,9 +29,8 @@
  *    page ids are out of range gets NaN outputs instead of a memory fault.
  *  - Results are deterministic: no atomics, fixed reduction order; the
  *    order depends on logical token indices only, never on physical pages.
- *  - Calls are thread-safe. The only process-wide state is the diagnostic
- *    wait limit (mla_set_wait_limit) and the static array of the
- *    allocation-free decode entry point.
+ *  - Calls are thread-safe. The only process-wide state is the static array
+ *    of the allocation-free decode entry point.
  *
  * dtypes: MLA_F32 = IEEE binary32, MLA_BF16 = bfloat16, MLA_FP8_E4M3 = OCP
  * E4M3FN (bias 7, max 448, no infinities) with one fp32 scale per token.
@@ -214,7 +213,7 @@ typedef struct mla_decode_args {
   int64_t total_tokens;     /* host hint: sum of seq_lens (0 = unknown) */
   float softmax_scale;      /* 1/sqrt(d_h + d_r) for DeepSeek-V2 (eq. 18) */
   int32_t heads_per_wg;     /* query rows (token, head pairs) per workgroup:
-                               0 = the kernel's own (BF16 pools 128, FP8 64,
+                               0 = the kernel's own (BF16 and FP8 pools 128,
                                F32 1; mla_decode_plan reports it), else it
                                must equal that value (MLA_ERR_UNSUPPORTED) */
   int64_t q_lat_stride;     /* row stride of q_lat (0: d_c), >= d_c */
@@ -266,11 +265,10 @@ int mla_decode_plan(const mla_decode_args* args, int* split_tokens, int* n_split
  *   u    = sum_s a_s c_s            (latent-space aggregate, W^UV not applied)
  *   lse  = ln sum_s exp(z_s)
  * F32 caches run an fp32 kernel; BF16 caches run bf16 MFMA with fp32 softmax
- * and accumulation; FP8_E4M3 latents stay fp8 in HBM and LDS and are widened
- * exactly to bf16 in registers for bf16 MFMA (q_lat is not quantized), the
- * per-token scale applied in fp32 to the latent score and to the weight:
- *   z_s = (scale_s * (q_lat . code_s) + q_rope . k^R_s) * softmax_scale
- *   u   = sum_s (a_s * scale_s) code_s
+ * and accumulation; FP8_E4M3 latents stay fp8 in HBM (half the bytes read)
+ * and are widened in LDS, once per tile, to c_s = bf16(scale_s * code_s)
+ * (the product in fp32, rounded to nearest even), which then takes the
+ * bf16 path (q_lat is not quantized).
  */
 int mla_decode_paged(const mla_decode_args* args, void* stream);
 
@@ -301,16 +299,6 @@ int mla_decode_paged_noalloc(const mla_decode_args* args, void* stream);
  */
 int mla_stream_read(const void* src, size_t bytes, void* sink, void* stream);
 
-/*
- * mla_set_wait_limit -- diagnostic: the number of polls (each followed by a
- * short sleep) a bounded wait inside a decode kernel makes before it gives
- * up; the fp8 kernel's waves wait so for their partner wave's tile maxima. A
- * wait that gives up marks its work unit, whose outputs (u and lse, or its
- * partials) become NaN, and the kernel exits normally. 0 makes every such
- * wait give up at once (how the failure path is tested). Process-wide,
- * default 1 << 20; returns the previous value, or -1 for a negative one.
- */
-int mla_set_wait_limit(int polls);
 
 /*
  * mla_out_proj -- each head's value up-projection applied after aggregation

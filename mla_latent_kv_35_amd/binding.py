@@ -89,8 +89,6 @@ _lib.mla_decode_plan.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.POINTER(_i),
                                  ctypes.POINTER(ctypes.c_size_t)]
 _lib.mla_decode_paged.restype = _i
 _lib.mla_decode_paged.argtypes = [ctypes.POINTER(DecodeArgs), _vp]
-_lib.mla_set_wait_limit.restype = _i
-_lib.mla_set_wait_limit.argtypes = [_i]
 _lib.mla_stream_read.restype = _i
 _lib.mla_stream_read.argtypes = [_vp, ctypes.c_size_t, _vp, _vp]
 _lib.mla_decode_paged_noalloc.restype = _i
@@ -116,7 +114,7 @@ _lib.mla_absorb_q_rope.argtypes = [_vp, _vp, _vp, _i, _i, _vp, _vp, _i, _vp, _i,
 
 EXPORTED = ["mla_status_str", "mla_abi_version", "mla_absorb_q", "mla_rope",
             "mla_decode_plan", "mla_decode_paged", "mla_decode_paged_noalloc", "mla_stream_read",
-            "mla_set_wait_limit", "mla_out_proj", "mla_cache_append",
+            "mla_out_proj", "mla_cache_append",
             "mla_rope_freq", "mla_yarn_frequencies", "mla_yarn_mscale", "mla_expand_kv",
             "mla_prefill_attn", "mla_absorb_q_rope"]
 
@@ -453,14 +451,6 @@ def decode_paged_noalloc(q_lat: torch.Tensor, q_rope: torch.Tensor, cache: Paged
     a.out, a.lse = _ptr(out), _ptr(lse)
     _check("mla_decode_paged_noalloc", _lib.mla_decode_paged_noalloc(ctypes.byref(a), _stream(stream)))
     return out, lse
-
-
-def set_wait_limit(polls: int) -> int:
-    """Polls a bounded in-kernel wait makes before it gives up; returns the previous value."""
-    prev = _lib.mla_set_wait_limit(polls)
-    if prev < 0:
-        raise ValueError(polls)
-    return prev
 
 
 def stream_read(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libmla.so")
 ARCH = "gfx950"
 
-SOURCES = ["mla_api.hip", "decode_pipe.hip", "decode_mfma.hip", "decode_simple.hip", "combine.hip",
+SOURCES = ["mla_api.hip", "decode_pipe.hip", "decode_simple.hip", "combine.hip",
            "rope.hip", "absorb.hip", "out_proj.hip", "append.hip", "prefill.hip",
            "gemm_nt.hip", "probe.hip"]
 
@@ -37,7 +37,6 @@ COMMON_FLAGS = [
 # accumulators in VGPRs: its rare accumulator rescale is plain VALU work there,
 # and the query fragments (MFMA B operands) can live in AGPRs.
 EXTRA_FLAGS = {
-    "decode_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

@@ -1,5 +1,5 @@
-// Paged absorbed-MLA decode on gfx950 MFMA for bf16 caches, software
-// pipelined across tiles.
+// Paged absorbed-MLA decode on gfx950 MFMA for bf16 and fp8 caches,
+// software pipelined across tiles.
 //
 // A workgroup of four waves (one per SIMD) owns a work unit: sequence b,
 // split k and 128 query rows, 32 per wave. The split's cache streams through
@@ -31,6 +31,16 @@
 // copy never reads past the sequence: slots beyond its last token repeat the
 // last token, and the mask gives them weight exactly 0.
 //
+// fp8 caches (E4M3FN codes with one fp32 scale per token) run the same
+// schedule on bf16 tiles: the copies land the codes of a tile in a staging
+// buffer and its scales in one of two scale buffers, both private to the
+// wave that copied them (each wave copies and widens its own 8 tokens), the
+// rope rows straight in the tile buffer; during the step before the tile is
+// scored the wave widens its codes to bf16(scale x code) in the tile buffer,
+// and each pair of rows is copied again (the next tile's) once its codes are
+// in registers. Three tile buffers: s (aggregation), s + 1 (score), s + 2
+// (being widened).
+//
 // The unit ends by writing either u = U / l and lse (one split), or partials
 // for the log-sum-exp combine: bf16 u = U / l with fp32 (m, l) when the
 // output is bf16, else fp32 (m, l, U).
@@ -46,18 +56,30 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kTile = 32;
 constexpr int kRows = 128;                 // query rows per workgroup, 32 per wave
-constexpr int kNB = 4;                     // tile buffers
-constexpr int kLatRow = 1024;              // bytes of one token's latent
+constexpr int kLatRow = 1024;              // bytes of one token's bf16 latent
 constexpr int kRopeOff = kTile * kLatRow;  // rope rows of 128 B
 constexpr int kTileBytes = kRopeOff + kTile * 128;
-constexpr int kOffIds = kNB * kTileBytes;
-// the first kQInLds query k-steps of every wave live in LDS, not registers
-constexpr int kQInLds = 2;
-constexpr int kOffQ = kOffIds + kMaxSplitPages * 4;
-constexpr int kLdsBytes = kOffQ + 4 * kQInLds * 1024;
-static_assert(kLdsBytes <= 163840, "LDS budget");
-constexpr int kCopies = 9;                 // copies per wave and tile
+constexpr int kLat8 = 512;                 // bytes of one token's fp8 latent
+constexpr int kStageScale = kTile * kLat8; // two buffers of staged scales follow the codes
+constexpr int kStageBytes = kStageScale + 2 * kTile * 4;
 constexpr int kSlots = 68;                 // MFMAs of a steady-state step
+
+// LDS layout: tile buffers, the fp8 staging buffer, the split's page ids
+// and the first kQInLds query k-steps of every wave (kept in LDS, not
+// registers).
+template <bool FP8>
+struct Lay {
+  static constexpr int kNB = FP8 ? 3 : 4;                 // tile buffers
+  static constexpr int kOffStage = kNB * kTileBytes;
+  static constexpr int kOffIds = kOffStage + (FP8 ? kStageBytes : 0);
+  static constexpr int kQInLds = FP8 ? 7 : 2;
+  static constexpr int kOffQ = kOffIds + kMaxSplitPages * 4;
+  static constexpr int kLdsBytes = kOffQ + 4 * kQInLds * 1024;
+  // copies per wave and tile: bf16 8 latent rows and the rope of 8 tokens;
+  // fp8 4 pairs of latent rows, the rope and the scales of 8 tokens
+  static constexpr int kCopies = FP8 ? 6 : 9;
+  static_assert(kLdsBytes + 256 <= 163840, "LDS budget (with the barrier reduction's)");
+};
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -127,10 +149,34 @@ __host__ __device__ constexpr int head_stage_at(int i) {
 __host__ __device__ constexpr int tail_stage_slot(int st) {
   return st == 6 ? 0 : st == 7 ? 0 : st == 8 ? 1 : 1;
 }
-// copy slots: op o of the step's nine copies follows MFMA 5 o + 4
-__host__ __device__ constexpr int copy_at(int i) {
-  return (i >= 4 && (i - 4) % 5 == 0 && (i - 4) / 5 < kCopies) ? (i - 4) / 5 : -1;
+// bf16 copy slots: op o of the step's nine copies follows MFMA 5 o + 4
+__host__ __device__ constexpr int copy_at16(int i) {
+  return (i >= 4 && (i - 4) % 5 == 0 && (i - 4) / 5 < 9) ? (i - 4) / 5 : -1;
 }
+// fp8 widening of the tile scored next, piece j (2 tokens of the wave) at
+// slots 4 + 8j (read its codes and scale), 7 + 8j and 10 + 8j (widen and
+// write a half); the copies: the scales (op 5) at slot 2, the rope (op 4)
+// at slot 3, latent pair j (op j) at slot 7 + 8j, after the half widened
+// there has consumed the pair's staged codes.
+constexpr int kConvFrom = 4;
+__host__ __device__ constexpr int conv_at(int i) {
+  return (i >= kConvFrom && i < kConvFrom + 32 && (i - kConvFrom) % 8 < 7 &&
+          (i - kConvFrom) % 8 % 3 == 0)
+             ? 3 * ((i - kConvFrom) / 8) + (i - kConvFrom) % 8 / 3
+             : -1;
+}
+__host__ __device__ constexpr int copy_at8(int i) {
+  return i == 2 ? 5 : i == 3 ? 4 : (i >= 7 && (i - 7) % 8 == 0 && (i - 7) / 8 < 4) ? (i - 7) / 8 : -1;
+}
+// Before the read of piece j, at most five of the wave's copies may fly:
+// the previous step's pairs j + 1..3 and this step's scales, rope and pairs
+// 0..j - 1; so the previous step's pair j and scales have landed.
+constexpr int kConvInFlight = 5;
+static_assert(conv_at(4) == 0 && conv_at(7) == 1 && conv_at(10) == 2 && conv_at(12) == 3 &&
+                  conv_at(34) == 11 && conv_at(36) == -1 && conv_at(5) == -1,
+              "widening slots");
+static_assert(copy_at8(2) == 5 && copy_at8(3) == 4 && copy_at8(7) == 0 && copy_at8(31) == 3 &&
+                  copy_at8(39) == -1, "fp8 copy slots");
 // the page id for the next step's copies is read from LDS after slot 30 and
 // moved to a scalar after slot 40
 constexpr int kIdRead = 30, kIdUse = 40;
@@ -171,9 +217,15 @@ __device__ void write_uniform(const DecodeParams& p, int b, int k, int row0, flo
   }
 }
 
+template <bool FP8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_pipe_kernel(DecodeParams p) {
-  __shared__ __attribute__((aligned(16))) char smem_raw[kLdsBytes];
+  using LY = Lay<FP8>;
+  constexpr int kNB = LY::kNB;
+  constexpr int kQInLds = LY::kQInLds;
+  constexpr int kOffQ = LY::kOffQ;
+  constexpr int kCopies = LY::kCopies;
+  __shared__ __attribute__((aligned(16))) char smem_raw[LY::kLdsBytes];
   lds_char* const smem = (lds_char*)smem_raw;
 
   const int bid = blockIdx.x;
@@ -243,7 +295,7 @@ void decode_pipe_kernel(DecodeParams p) {
   // visible-token limit of the row: s < min(L - T + t + 1, tok1)
   const int lim = min(L - p.T + (my_row < p.R ? my_row / p.H : 0) + 1, tok1);
 
-  int* const ids = (int*)(smem_raw + kOffIds);  // page ids of the split (filled below)
+  int* const ids = (int*)(smem_raw + LY::kOffIds);  // page ids of the split (filled below)
   // copies: latent row 4w + 16g + j takes chunk lane ^ (4j + w) (its gsw);
   // rope token 8w + lane / 8 takes chunk (lane & 7) ^ swz_rope(token)
   const uint32_t lane16 = (uint32_t)lane << 4;
@@ -252,10 +304,12 @@ void decode_pipe_kernel(DecodeParams p) {
   // ---- page copies ------------------------------------------------------------
   const char* const ckv_base = (const char*)p.ckv;
   const char* const kr_base = (const char*)p.kr;
+  const char* const scale_base = (const char*)p.ckv_scale;
   struct TileSrc {
     const char* cp;
     const char* rp;
-    int lds, sb, last;
+    const char* sp;    // fp8: the page's scales
+    int lds, ssc, sb, last;
   };
   // tile jt of the split into buffer jdst: a tile past the split's end
   // re-reads the split's last tile
@@ -267,9 +321,11 @@ void decode_pipe_kernel(DecodeParams p) {
     const int t0 = tok0 + jc * kTile;                  // first token of the tile
     const size_t idc = (size_t)id;                     // checked in [0, n_pages)
     TileSrc ts;
-    ts.cp = ckv_base + idc * (kPage * kLatRow);
+    ts.cp = ckv_base + idc * (kPage * (FP8 ? kLat8 : kLatRow));
     ts.rp = kr_base + idc * (kPage * kDr * 2);
+    ts.sp = FP8 ? scale_base + idc * (kPage * 4) : nullptr;
     ts.lds = (jdst % kNB) * kTileBytes;
+    ts.ssc = LY::kOffStage + kStageScale + (jdst & 1) * (kTile * 4);
     ts.sb = t0 & (kPage - 1);
     ts.last = min(L - 1 - (t0 - ts.sb), kPage - 1);    // in [0, 63]
     return ts;
@@ -279,9 +335,42 @@ void decode_pipe_kernel(DecodeParams p) {
   // form assumes every slot of the tile holds a token (the copies of a row
   // group share one base, the row's offset rides in the instruction); the
   // safe form reads page slot min(sb + t, last) for slot sb + t.
+  // fp8 (ops 0-5): ops 0-3 the latent codes of tokens 8w + 2 op (lanes 0-31)
+  // and 8w + 2 op + 1 (lanes 32-63) into the wave's staging rows, op 4 the
+  // rope rows as for bf16, op 5 the scales of tokens 8w..8w + 7 (lanes 0-7).
   auto copy_op = [&](const TileSrc& ts, int op, auto safe_c) __attribute__((always_inline)) {
     constexpr bool kSafe = decltype(safe_c)::value;
     const lds_char* const dst = smem + ts.lds;
+    if constexpr (FP8) {
+      if (op < 4) {
+        const int t0 = 8 * w + 2 * op;
+        if constexpr (!kSafe) {
+          const char* const gb = ts.cp + (size_t)(ts.sb + 8 * w) * kLat8;
+          const lds_char* const lb = smem + LY::kOffStage + 8 * w * kLat8;
+          if (op == 0) dma_copy16_off<0>(gb, lane16, lb);
+          else if (op == 1) dma_copy16_off<1024>(gb, lane16, lb);
+          else if (op == 2) dma_copy16_off<2048>(gb, lane16, lb);
+          else dma_copy16_off<3072>(gb, lane16, lb);
+        } else {
+          const int r = min(ts.sb + t0 + (lane >> 5), ts.last);
+          dma_copy16_m0(ts.cp, ((uint32_t)r * kLat8) + ((uint32_t)(lane & 31) << 4),
+                        smem + LY::kOffStage + t0 * kLat8);
+        }
+      } else if (op == 4) {
+        if constexpr (!kSafe) {
+          dma_copy16_m0(ts.rp + (size_t)(ts.sb + 8 * w) * 128, rope_v, dst + kRopeOff + w * 1024);
+        } else {
+          const int t = 8 * w + (lane >> 3);
+          dma_copy16_m0(ts.rp, ((uint32_t)min(ts.sb + t, ts.last) << 7) + (rope_v & 127u),
+                        dst + kRopeOff + w * 1024);
+        }
+      } else if (lane < 8) {
+        const uint32_t r = kSafe ? (uint32_t)min(ts.sb + 8 * w + lane, ts.last)
+                                 : (uint32_t)(ts.sb + 8 * w + lane);
+        dma_copy4_m0(ts.sp, r << 2, smem + ts.ssc + 32 * w);
+      }
+      return;
+    }
     if (op < 8) {
       const int g = op >> 2, j = op & 3;
       const int t0 = 4 * w + 16 * g;
@@ -310,10 +399,57 @@ void decode_pipe_kernel(DecodeParams p) {
   auto read_id = [&](int jt) __attribute__((always_inline)) -> int {
     return __builtin_amdgcn_readfirstlane(ids[page_slot(jt)]);
   };
-  auto copy_tile = [&](int jt, int jdst) __attribute__((always_inline)) {
+  // copy ops [op0, op1) of tile jt into buffer jdst
+  auto copy_tile = [&](int jt, int jdst, int op0, int op1) __attribute__((always_inline)) {
     const TileSrc ts = tile_src(jt, jdst, read_id(jt));
 #pragma clang loop unroll(full)
-    for (int op = 0; op < kCopies; ++op) copy_op(ts, op, std::true_type{});
+    for (int op = 0; op < kCopies; ++op)
+      if (op >= op0 && op < op1) copy_op(ts, op, std::true_type{});
+  };
+
+  // ---- fp8 widening -------------------------------------------------------------
+  // Piece j of the wave: token t = 8w + 2j + hb (hb = lane >> 5), codes
+  // 16 p .. 16 p + 15 (p = lane & 31), i.e. bf16 chunks 2p and 2p + 1 of the
+  // tile row. Op 3j reads the codes and the token's scale, ops 3j + 1 and
+  // 3j + 2 widen and write chunk 2p + hf (hf = op - 3j - 1): bf16(scale x
+  // code), in the tile's swizzled layout. The chunk's position in the row,
+  // (2p + hf) ^ gsw(t), splits into a lane part X = 2p ^ 4hb and a part
+  // C = 8 (j & 1) ^ ((2w + (j >> 1)) & 3) ^ hf that is uniform over the wave,
+  // so the write address is (row base of 8w + hb, plus 16 X) ^ 16 C, plus
+  // 2048 j: X, and the tile buffer's base (a multiple of 1 KB), leave bits
+  // 4-9 to the XOR alone.
+  const int cv_read = LY::kOffStage + 8 * w * kLat8 + lane * 16;   // + 1024 j
+  const int cv_scale = 32 * w + 4 * (lane >> 5);                    // + scale buffer + 8 j
+  const int cv_row = ((lane >> 5) << 10) + ((2 * (lane & 31)) ^ (4 * (lane >> 5))) * 16 +
+                     8 * w * kLatRow;                               // + tile buffer
+  u32x4_t craw = {0u, 0u, 0u, 0u};
+  float csc = 0.f;
+  // sa: scale buffer + cv_scale; za: tile buffer + cv_row
+  auto conv_op = [&](int op, int sa, int za) __attribute__((always_inline)) {
+    const int j = op / 3, part = op % 3;
+    if (part == 0) {
+      craw = *(const MLA_LDS u32x4_t*)(smem + cv_read + 1024 * j);
+      csc = *(const MLA_LDS float*)(smem + sa + 8 * j);
+      return;
+    }
+    const int hf = part - 1;
+    typedef float f2_t __attribute__((ext_vector_type(2)));
+    uint32_t o[4];
+#pragma clang loop unroll(full)
+    for (int d = 0; d < 2; ++d) {
+      const f2_t lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(craw[2 * hf + d], 1.0f, false);
+      const f2_t hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(craw[2 * hf + d], 1.0f, true);
+      o[2 * d] = pack_bf16x2(lo[0] * csc, lo[1] * csc);
+      o[2 * d + 1] = pack_bf16x2(hi[0] * csc, hi[1] * csc);
+    }
+    const int C = (8 * (j & 1)) ^ ((2 * w + (j >> 1)) & 3) ^ hf;
+    *(MLA_LDS u32x4_t*)(smem + (za ^ (C << 4)) + 2048 * j) = (u32x4_t){o[0], o[1], o[2], o[3]};
+  };
+  auto conv_tile = [&](int jt) __attribute__((always_inline)) {
+    const int sa = LY::kOffStage + kStageScale + (jt & 1) * (kTile * 4) + cv_scale;
+    const int za = (jt % kNB) * kTileBytes + cv_row;
+#pragma clang loop unroll(full)
+    for (int op = 0; op < 12; ++op) conv_op(op, sa, za);
   };
 
   // ---- the first two tiles (both in the split's first page) go out now; a
@@ -326,8 +462,9 @@ void decode_pipe_kernel(DecodeParams p) {
     const TileSrc t0s = tile_src(0, 0, id0), t1s = tile_src(1, 1, id0);
 #pragma clang loop unroll(full)
     for (int op = 0; op < kCopies; ++op) copy_op(t0s, op, std::true_type{});
+    // (fp8: tile 1's codes wait for the staging rows that tile 0's occupy)
 #pragma clang loop unroll(full)
-    for (int op = 0; op < kCopies; ++op) copy_op(t1s, op, std::true_type{});
+    for (int op = FP8 ? 4 : 0; op < kCopies; ++op) copy_op(t1s, op, std::true_type{});
   }
   // the group's earliest limit: tiles ending before it need no mask
   const int lim_min = min(L - p.T + min(row0, p.R - 1) / p.H + 1, tok1);
@@ -541,6 +678,9 @@ void decode_pipe_kernel(DecodeParams p) {
   // (s + 3) % 4. Returns the page id for the next step's copies.
   auto step = [&](int s, int cid, auto safe_c) __attribute__((always_inline)) -> int {
     const TileSrc cts = tile_src(s + 3, s + 3, cid);
+    // fp8: tile s + 2 is widened from the staging rows into its tile buffer
+    const int csa = LY::kOffStage + kStageScale + ((s + 2) & 1) * (kTile * 4) + cv_scale;
+    const int cza = ((s + 2) % kNB) * kTileBytes + cv_row;
     bf16x8_t qL[kQInLds];
 #pragma clang loop unroll(full)
     for (int j = 0; j < kQInLds; ++j) qL[j] = qop(j);
@@ -562,7 +702,14 @@ void decode_pipe_kernel(DecodeParams p) {
         U[e2 & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % kDist], P[e2 >> 4], U[e2 & 15], 0, 0, 0);
       }
       if (i + kDist < kSlots) fetch(i + kDist);
-      if (copy_at(i) >= 0) copy_op(cts, copy_at(i), safe_c);
+      if constexpr (FP8) {
+        const int cv = conv_at(i);
+        if (cv >= 0 && cv % 3 == 0) vm_wait<kConvInFlight>();   // the piece's codes and scales
+        if (cv >= 0) conv_op(cv, csa, cza);
+        if (copy_at8(i) >= 0) copy_op(cts, copy_at8(i), safe_c);
+      } else {
+        if (copy_at16(i) >= 0) copy_op(cts, copy_at16(i), safe_c);
+      }
       if (i == kIdRead) idv = ids[page_slot(s + 4)];
       if (i == kIdUse) nid = __builtin_amdgcn_readfirstlane(idv);
       if (i == kLastScore + 1) score_fence(SA, SB);
@@ -615,10 +762,20 @@ void decode_pipe_kernel(DecodeParams p) {
     // tiles 0 and 1 (a split of one tile re-reads it into buffer 1); the
     // first pass's went out before the queries loaded
     if (pass > 0) {
-      copy_tile(0, 0);
-      copy_tile(1, 1);
+      copy_tile(0, 0, 0, kCopies);
+      copy_tile(1, 1, FP8 ? 4 : 0, kCopies);
     }
-    vm_wait<kCopies>();
+    if constexpr (FP8) {
+      // tiles 0 and 1 widened (each wave its own tokens) before the barrier;
+      // tile 1's codes go out once tile 0's have been widened
+      vm_wait<0>();
+      conv_tile(0);
+      copy_tile(1, 1, 0, 4);
+      vm_wait<0>();
+      conv_tile(1);
+    } else {
+      vm_wait<kCopies>();
+    }
     if (pass == 0) {
       // (after the wait: an earlier store would wait for the first copies
       // before the queries were needed)
@@ -632,7 +789,7 @@ void decode_pipe_kernel(DecodeParams p) {
     int cid = read_id(3);
     lead_reads();
     vm_wait<kCopies>();
-    lds_barrier_keep<2 * kLeadG>();                    // tile 1 resident
+    lds_barrier_keep<2 * kLeadG>();                    // tile 1 resident (bf16)
     // after step s: tile s + 2 resident (the copies of tile s + 3 may fly),
     // tile s's buffer free; the lead reads of step s + 1 may still fly
     const int n_fast = max(n_tiles - 4, 0);            // steps whose copy tile is full
@@ -716,8 +873,11 @@ void decode_pipe_kernel(DecodeParams p) {
 
 }  // namespace
 
-hipError_t launch_decode_pipe(const DecodeParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(decode_pipe_kernel, dim3(p.per_xcd * kNumXcd), dim3(kThreads), 0, s, p);
+hipError_t launch_decode_pipe(const DecodeParams& p, bool fp8, hipStream_t s) {
+  if (fp8)
+    hipLaunchKernelGGL(decode_pipe_kernel<true>, dim3(p.per_xcd * kNumXcd), dim3(kThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL(decode_pipe_kernel<false>, dim3(p.per_xcd * kNumXcd), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 

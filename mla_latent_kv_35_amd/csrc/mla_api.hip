@@ -3,7 +3,6 @@
 #include <math.h>
 
 #include <algorithm>
-#include <atomic>
 #include <mutex>
 
 #include "mla_extra.h"
@@ -65,7 +64,7 @@ int rope_strides(const void* x_in, const void* x_out, int n_tok, int n_heads, in
 }
 
 // Query rows per workgroup of the decode kernel for this latent pool dtype.
-int kernel_rows(int ckv_dt) { return ckv_dt == MLA_BF16 ? 128 : ckv_dt == MLA_FP8_E4M3 ? 64 : 1; }
+int kernel_rows(int ckv_dt) { return ckv_dt == MLA_F32 ? 1 : 128; }
 
 struct Plan {
   int split_tokens = 0;
@@ -153,14 +152,6 @@ Plan make_plan(const mla_decode_args* a) {
   return pl;
 }
 
-}  // namespace
-}  // namespace mla
-
-// Polls a bounded in-kernel wait makes before it gives up (and the unit's
-// outputs become NaN); changed only through mla_set_wait_limit.
-namespace mla {
-namespace {
-std::atomic<int> g_spin_limit{1 << 20};
 }  // namespace
 }  // namespace mla
 
@@ -405,7 +396,6 @@ int mla_decode_paged(const mla_decode_args* a, void* stream) {
   p.max_seq_len = a->max_seq_len;
   p.out_bf16 = a->out_dt == MLA_BF16;
   p.scale_log2 = a->softmax_scale * kLog2e;
-  p.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
   p.q_lat_stride = a->q_lat_stride ? (long)a->q_lat_stride : kDc;
   p.q_rope_stride = a->q_rope_stride ? (long)a->q_rope_stride : kDr;
   const int64_t units = (int64_t)a->B * pl.n_split * pl.G;
@@ -416,8 +406,7 @@ int mla_decode_paged(const mla_decode_args* a, void* stream) {
   const hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if (a->ckv_dt == MLA_F32) e = launch_decode_simple_f32(p, s);
-  else if (a->ckv_dt == MLA_BF16) e = launch_decode_pipe(p, s);
-  else e = launch_decode_mfma_fp8(p, s);
+  else e = launch_decode_pipe(p, a->ckv_dt == MLA_FP8_E4M3, s);
   if (e != hipSuccess) return MLA_ERR_LAUNCH;
   if (pl.n_split > 1) {
     CombineParams c{};
@@ -471,10 +460,6 @@ int mla_decode_paged_noalloc(const mla_decode_args* args, void* stream) {
   return mla_decode_paged(&a, stream);
 }
 
-int mla_set_wait_limit(int polls) {
-  if (polls < 0) return -1;
-  return g_spin_limit.exchange(polls);
-}
 
 int mla_stream_read(const void* src, size_t bytes, void* sink, void* stream) {
   if (!src || !sink) return MLA_ERR_NULL;

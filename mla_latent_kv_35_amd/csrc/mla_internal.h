@@ -14,7 +14,6 @@ constexpr int kPage = 64;
 constexpr int kDc = 512;
 constexpr int kDr = 64;
 constexpr int kDh = 128;
-constexpr int kRowsPerGroup = 64;   // query rows per decode workgroup (MFMA kernel)
 constexpr int kMaxSplitPages = 1024; // pages of one split (MFMA kernel keeps their ids in LDS)
 constexpr int kNumXcd = 8;          // MI355X: 8 XCDs, workgroups dispatched round-robin
 constexpr float kLog2e = 1.4426950408889634f;
@@ -42,7 +41,6 @@ struct DecodeParams {
   int n_units;              // work units actually present
   int per_xcd;              // grid = per_xcd * 8 (XCD-major unit numbering)
   float scale_log2;         // softmax_scale * log2(e)
-  int spin_limit;           // polls of a bounded wait before it gives up (fp8 kernel)
   long q_lat_stride;        // elements between consecutive query rows of q_lat
   long q_rope_stride;       // ... and of q_rope
 };
@@ -68,10 +66,10 @@ struct CombineParams {
 
 
 
-hipError_t launch_decode_mfma_fp8(const DecodeParams& p, hipStream_t s);
 hipError_t launch_decode_simple_f32(const DecodeParams& p, hipStream_t s);
-// bf16 latent and rope pools, 128 query rows per workgroup
-hipError_t launch_decode_pipe(const DecodeParams& p, hipStream_t s);
+// bf16 (fp8: E4M3FN latent codes with per-token scales) latent pool, bf16
+// rope pool, 128 query rows per workgroup
+hipError_t launch_decode_pipe(const DecodeParams& p, bool fp8, hipStream_t s);
 hipError_t launch_stream_read(const void* src, size_t bytes, void* sink, hipStream_t s);
 hipError_t launch_combine(const CombineParams& p, hipStream_t s);
 // combine fused with the value up-projection; needs p.w_uv, p.o, n_split <= 64

@@ -60,7 +60,7 @@ def test_plan_for_the_five_workloads(B):
     # 128K: 4 pairs x 64 splits
     assert B.decode_plan(_args(B, B=4, n_pages=8192, max_pages_per_seq=2048,
                                    max_seq_len=131072))[:2] == (2048, 64)
-    # two-token fp8: 4 row groups x 128 sequences, no split
+    # two-token fp8: 2 row groups of 128 x 128 sequences, no split
     st, ns, ws = B.decode_plan(_args(B, B=128, T=2, ckv_dt=B.MLA_FP8_E4M3, n_pages=16384,
                                      max_pages_per_seq=128, max_seq_len=8192))
     assert ns == 1 and ws == 0
@@ -97,8 +97,8 @@ def test_plan_rejects_bad_shapes(B, field, value, status):
 
 
 def test_plan_reports_rows_per_workgroup_and_accepts_strides(B):
-    # the kernel's own rows per workgroup: bf16 pools 128, fp8 64, fp32 1
-    for kw, rows in ((dict(), 128), (dict(ckv_dt=B.MLA_FP8_E4M3), 64),
+    # the kernel's own rows per workgroup: bf16 and fp8 pools 128, fp32 1
+    for kw, rows in ((dict(), 128), (dict(ckv_dt=B.MLA_FP8_E4M3), 128),
                      (dict(q_dt=0, ckv_dt=0, kr_dt=0, out_dt=0), 1)):
         assert B.decode_plan_full(_args(B, **kw))[2] == rows
         # naming it explicitly is the same plan
@@ -263,12 +263,3 @@ def test_stream_read_rejects_misaligned(B):
     assert lib.mla_stream_read(8, 16, 16, None) == 4       # src not 16-byte aligned
     assert lib.mla_stream_read(16, 16, 8, None) == 4       # sink not 16-byte aligned
     assert lib.mla_stream_read(16, 0, 16, None) == 0       # nothing to read
-
-
-def test_wait_limit_setter(B):
-    lib = B.lib()
-    prev = lib.mla_set_wait_limit(12345)
-    assert prev == 1 << 20
-    assert lib.mla_set_wait_limit(prev) == 12345
-    assert lib.mla_set_wait_limit(-1) == -1
-    assert lib.mla_set_wait_limit(prev) == prev

@@ -139,8 +139,8 @@ def test_small_fp32_parity(mla, split):
 @pytest.mark.parametrize("kw", SMALL)
 @pytest.mark.parametrize("split", [0, 64, 192])
 def test_small_fp8_parity(mla, kw, split):
-    # fp8 latent cache with per-token scales; the codes are widened exactly to
-    # bf16 for the MFMA and q_lat stays bf16
+    # fp8 latent cache with per-token scales; the codes are widened to
+    # bf16(scale x code) in LDS for the bf16 MFMA and q_lat stays bf16
     cfg = synth.small_config(seed=300 + kw["B"] + kw["seq_len"], ckv_dt="fp8", **kw)
     check_against_oracle(mla, synth.make_inputs(cfg), split_tokens=split)
 
@@ -427,29 +427,6 @@ def test_stream_read_probe_runs(mla):
     mla.stream_read(src, sink)
     torch.cuda.synchronize()
     assert int(sink.sum()) == 0       # the folded loads of all-ones bytes never hit the sentinel
-
-
-def test_fp8_partner_wait_gives_up_loudly(mla):
-    """The fp8 kernel's bounded partner wait: with a limit of 0 every wait
-    gives up, every unit's outputs turn NaN and the kernels exit normally;
-    with the limit restored the same call is correct again."""
-    cfg = synth.small_config(B=2, H=64, T=1, seq_len=300, ckv_dt="fp8", seed=91)
-    inp = synth.make_inputs(cfg)
-    d = mla.upload(inp)
-    q_lat = mla.absorb_q(d.q_nope, d.w_uk)
-    q_rot = mla.rope(d.q_rope, d.positions)
-    for split in (0, 64):
-        prev = mla.set_wait_limit(0)
-        try:
-            u, lse = mla.decode_paged(q_lat, q_rot, d.cache, 1, d.softmax_scale, split_tokens=split)
-            torch.cuda.synchronize()
-        finally:
-            mla.set_wait_limit(prev)
-        assert torch.isnan(u.float()).all() and torch.isnan(lse).all(), split
-        u2, _ = mla.decode_paged(q_lat, q_rot, d.cache, 1, d.softmax_scale, split_tokens=split)
-        torch.cuda.synchronize()
-        ref = O.decode_step(inp)
-        assert row_rel(host(u2), np.stack([ref[b]["u"][0] for b in ref])) <= TOL["fp8"]
 
 
 # --------------------------------------------------------------------------
