@@ -60,8 +60,7 @@ def copy_probe(mib: int) -> None:
 
 def kernel_source_digest() -> str:
     h = hashlib.sha256()
-    for f in ("decode_pipe.hip", "decode_mfma.hip", "combine.hip", "dma.h", "mla_device.h",
-              "mla_internal.h"):
+    for f in ("decode_pipe.hip", "combine.hip", "dma.h", "mla_device.h", "mla_internal.h"):
         with open(os.path.join(ROOT, "mla_latent_kv_35_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -325,8 +324,8 @@ def main():
                        "decode_hbm_over_read": round(achieved / read_gbps, 4)},
         "launch": "hip graph of %d steps per replay" % per_graph,
         "roofline": {
-            "kernel": ("mla_decode_paged: split-KV kernel (decode_pipe_kernel for bf16 pools, "
-                       "decode_mfma_kernel for fp8) + log-sum-exp combine, timed together"),
+            "kernel": ("mla_decode_paged: split-KV kernel (decode_pipe_kernel, bf16 and fp8 "
+                       "pools) + log-sum-exp combine, timed together"),
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": PEAK_HBM_GBPS,
