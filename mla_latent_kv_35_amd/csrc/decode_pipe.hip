@@ -247,7 +247,12 @@ void decode_pipe_kernel(DecodeParams p) {
 
   // ---- one round trip: the sequence length, the split's page ids and the
   // absorbed queries load together (none of the addresses depends on L) ----
-  const int L_raw = p.seq_lens[b];
+  // L through a vector load (a laundered zero index): a scalar load would
+  // share lgkmcnt with the kernel-argument loads, and the first wait for an
+  // argument would then wait for L as well
+  int zero = 0;
+  asm volatile("" : "+v"(zero));
+  const int L_raw = p.seq_lens[b + zero];
   const int32_t* const btrow = p.block_table + (size_t)b * p.max_pages;
   const int pg_cap = min(p.split_tokens / kPage, p.max_pages - pg_begin);   // >= the split's pages
   int idr[kMaxSplitPages / kThreads];
@@ -275,6 +280,9 @@ void decode_pipe_kernel(DecodeParams p) {
       qB[ks] = live ? v : (bf16x8_t){0, 0, 0, 0, 0, 0, 0, 0};
     }
   }
+  // keep these loads above the branches on L below (sunk past them, they
+  // would wait a round trip for L before even being issued)
+  asm volatile("" ::: "memory");
 
   const int L = __builtin_amdgcn_readfirstlane(L_raw);
   const int tok1 = min(tok0 + p.split_tokens, L);
