@@ -511,3 +511,63 @@ def test_rope_token_and_head_strides(mla):
     for g in (got, got_odd):
         assert torch.equal(g.contiguous().view(torch.int16), want.view(torch.int16))
     assert torch.isnan(y[:, :, :32].float()).all() and torch.isnan(y[:, :, 96:].float()).all()
+
+
+# --------------------------------------------------------------------------
+# fp8 pools: the widening bf16(fp32(code) x fp32(scale)) is exact and stated
+# in the header, so a single visible token returns it bit for bit
+# --------------------------------------------------------------------------
+
+def _widened(inp, page, slot):
+    """bf16 bits of bf16(fp32(code) * fp32(scale)) for one cached fp8 token:
+    the code decoded by torch's E4M3FN cast, the product rounded to nearest
+    even in fp32, then to bf16."""
+    codes = torch.from_numpy(np.ascontiguousarray(inp.ckv[page, slot])).view(torch.float8_e4m3fn)
+    prod = codes.float().numpy() * np.float32(inp.ckv_scale[page, slot])
+    return synth.f32_to_bf16_bits(prod.astype(np.float32)).view(np.int16)
+
+
+def test_fp8_single_token_returns_widened_latent_bit_exact(mla):
+    inp = synth.make_inputs(synth.small_config(B=2, H=128, T=1, seq_len=1, ckv_dt="fp8", seed=23))
+    u, _ = _decode_u(mla, inp)
+    for b in range(2):
+        want = _widened(inp, inp.block_table[b, 0], 0)
+        assert np.all(u[b] == want[None, :]), b
+
+
+@pytest.mark.parametrize("target", [0, 7, 8, 31, 32, 63, 64, 127, 128, 191, 299])
+def test_fp8_one_hot_gather_bit_exact(mla, target):
+    """All weight on one token through the rope channel: u is that token's
+    widened latent exactly, wherever it sits in a tile (each wave widens 8
+    tokens in pieces of two), a page, a split or the ragged tail."""
+    inp = synth.make_inputs(synth.small_config(B=1, H=128, T=1, seq_len=300, permuted=True,
+                                               ckv_dt="fp8", seed=29))
+    inp.q_nope[...] = 0
+    inp.q_rope[...] = 0
+    inp.q_rope[:, :, 62] = synth.f32_to_bf16_bits(np.array([1000.0], np.float32))[0]
+    inp.kr[...] = 0
+    bt = inp.block_table[0]
+    inp.kr[bt[target // 64], target % 64, 62] = synth.f32_to_bf16_bits(np.array([4.0], np.float32))[0]
+    want = _widened(inp, bt[target // 64], target % 64)
+    for split in (0, 64, 128):
+        u, _ = _decode_u(mla, inp, split)
+        assert np.all(u[0] == want[None, :]), split
+
+
+@pytest.mark.parametrize("ckv_dt", ["bf16", "fp8"])
+@pytest.mark.parametrize("T", [1, 2])
+@pytest.mark.parametrize("seq_len", [2, 31, 33, 95])
+def test_short_sequences_parity(mla, ckv_dt, T, seq_len):
+    """Splits of one to three tiles (the prologue copies and widens two tiles
+    before the first score; shorter splits re-read their last tile), ragged
+    lengths down to T."""
+    seed = 400 + 10 * seq_len + T
+    while True:   # ragged lengths are drawn from [1, seq_len]; a valid batch has every L >= T
+        cfg = synth.small_config(B=3, H=32, T=T, seq_len=seq_len, ragged=True, permuted=True,
+                                 ckv_dt=ckv_dt, seed=seed)
+        inp = synth.make_inputs(cfg)
+        if inp.seq_lens.min() >= T:
+            break
+        seed += 1000
+    check_against_oracle(mla, inp)
+    check_against_oracle(mla, inp, split_tokens=64)
