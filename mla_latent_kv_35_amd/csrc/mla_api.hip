@@ -132,9 +132,11 @@ Plan make_plan(const mla_decode_args* a) {
     pl.split_tokens = (int)(std::max<int64_t>(sp, 1) * kPage);
   } else {
     // MFMA kernels: units of (sequence, split, row group). Uniform batches
-    // get one unit per CU; ragged ones four per CU so the uneven tails balance.
+    // get one unit per CU; ragged ones two per CU, so that the uneven tails
+    // balance (measured on the 64-sequence ragged batch: 1, 1.5, 3 and 4 per
+    // CU were slower, each unit paying its own start of about 6 us)
     const bool ragged = total * 10 < (int64_t)a->B * Lmax * 9;
-    const int64_t target = ragged ? 4 * kNumCu : kNumCu;
+    const int64_t target = ragged ? 2 * kNumCu : kNumCu;
     int64_t unit_pages = (pl.G * pages_total + target - 1) / target;
     unit_pages = std::max<int64_t>(unit_pages, 4);
     unit_pages = std::min<int64_t>(unit_pages, max_pages);

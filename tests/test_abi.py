@@ -64,7 +64,7 @@ def test_plan_for_the_five_workloads(B):
     st, ns, ws = B.decode_plan(_args(B, B=128, T=2, ckv_dt=B.MLA_FP8_E4M3, n_pages=16384,
                                      max_pages_per_seq=128, max_seq_len=8192))
     assert ns == 1 and ws == 0
-    # ragged: planned from the token total, about four units per CU
+    # ragged: planned from the token total, about two units per CU
     st, ns, ws = B.decode_plan(_args(B, B=64, n_pages=16522, max_pages_per_seq=497,
                                      max_seq_len=31804, total_tokens=1055283))
     assert st % 64 == 0 and ns == -(-31804 // st)
