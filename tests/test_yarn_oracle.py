@@ -102,3 +102,24 @@ def test_library_host_helpers_equal_oracle():
         B.yarn_frequencies(64, 10000.0, 0.5, 1.0, 32.0, 4096)      # factor < 1
     with pytest.raises(B.MlaError):
         B.yarn_frequencies(64, 10000.0, 40.0, 32.0, 1.0, 4096)     # beta <= alpha
+
+
+def test_ramp_bounds_and_constructed_edges():
+    """Every interpolated frequency lies between the fully slowed theta / s and
+    the plain theta, and is continuous at both edges of the ramp: windows
+    built so that one pair makes exactly alpha (exactly beta) turns give that
+    pair theta / s (theta), and a window a hair longer or shorter moves it
+    only a hair. A swapped alpha / beta or an inverted ramp fails these."""
+    d, base, s = 64, 10000.0, 40.0
+    th = plain(d, base)
+    for (a, b, L0) in ((1.0, 32.0, 4096), (0.5, 4.0, 1000), (2.0, 64.0, 32768)):
+        y = O.yarn_theta(d, base, s, a, b, L0)
+        assert np.all(y <= th * (1 + 1e-15)) and np.all(y >= th / s * (1 - 1e-15))
+    i = 20
+    for turns, want in ((1.0, th[i] / s), (32.0, th[i])):
+        L_edge = 2 * math.pi * turns / th[i]
+        y = O.yarn_theta(d, base, s, 1.0, 32.0, L_edge)
+        assert math.isclose(y[i], want, rel_tol=1e-12)
+        for eps in (1e-9, -1e-9):
+            y2 = O.yarn_theta(d, base, s, 1.0, 32.0, L_edge * (1 + eps))
+            assert abs(y2[i] - want) <= 1e-6 * want
