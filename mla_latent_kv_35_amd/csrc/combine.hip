@@ -263,7 +263,12 @@ __device__ __forceinline__ void store_u_row(const CombineParams& p, int row, int
 
 __global__ __launch_bounds__(64 * kWaveRows) void combine_wave_kernel(CombineParams p) {
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int row = __builtin_amdgcn_readfirstlane(blockIdx.x * kWaveRows + wv);  // b*R + r
+  // block b' of the rows runs on XCD b' / per_xcd (the hardware deals blocks
+  // to the 8 XCDs round-robin), the XCD whose split units wrote those rows'
+  // partials when the decode placed them the same way
+  const int per_xcd = gridDim.x / kNumXcd;
+  const int lb = (blockIdx.x % kNumXcd) * per_xcd + blockIdx.x / kNumXcd;
+  const int row = __builtin_amdgcn_readfirstlane(lb * kWaveRows + wv);  // b*R + r
   if (row >= p.rows) return;                      // the whole wave leaves; no barrier below
   const int rows[1] = {row};
   float u[1][8], lse[1];
@@ -369,7 +374,8 @@ hipError_t launch_combine_out(const CombineParams& p, hipStream_t s) {
 hipError_t launch_combine(const CombineParams& p, hipStream_t s) {
   if (p.n_split > kMaxSplitsLds) return hipErrorInvalidValue;
   if (p.n_split <= 64)
-    hipLaunchKernelGGL(combine_wave_kernel, dim3((p.rows + kWaveRows - 1) / kWaveRows),
+    hipLaunchKernelGGL(combine_wave_kernel,
+                       dim3(((p.rows + kWaveRows - 1) / kWaveRows + kNumXcd - 1) / kNumXcd * kNumXcd),
                        dim3(64 * kWaveRows), 0, s, p);
   else
     hipLaunchKernelGGL(combine_kernel, dim3(p.rows), dim3(kThreads), 0, s, p);
