@@ -379,8 +379,9 @@ def test_out_of_range_length_and_page_give_nan(mla):
 # HIP graph capture of the whole step: every replay equals the eager result
 # --------------------------------------------------------------------------
 
-def test_graph_replay_matches_eager(mla):
-    inp = _ragged(seed=61, B=4, seq_len=900)
+@pytest.mark.parametrize("ckv_dt", ["bf16", "fp8"])
+def test_graph_replay_matches_eager(mla, ckv_dt):
+    inp = _ragged(seed=61, B=4, seq_len=900, ckv_dt=ckv_dt)
     d = mla.upload(inp)
     eager = mla.decode_step(d, split_tokens=128)
     torch.cuda.synchronize()

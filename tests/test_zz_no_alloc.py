@@ -33,7 +33,9 @@ def test_noalloc_matches_workspace_entry_point(mla):
     torch.manual_seed(11)
     big = synth.small_config("noalloc_big", B=4, H=128, T=1, seq_len=3000, ragged=True, seed=21)
     small = synth.small_config("noalloc_small", B=2, H=64, T=2, seq_len=700, seed=22)
-    for cfg, split in ((big, 256), (small, 128)):
+    small8 = synth.small_config("noalloc_small_fp8", B=2, H=64, T=2, seq_len=700, seed=24,
+                                ckv_dt="fp8")
+    for cfg, split in ((big, 256), (small, 128), (small8, 64)):
         u_ref, lse_ref, u, lse, n_split, ws = _decode_both(mla, cfg, split)
         print(cfg.name, "splits", n_split, "workspace bytes", ws)
         assert n_split > 1 and ws > 0          # the partials go through the scratch array
