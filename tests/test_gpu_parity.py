@@ -180,11 +180,11 @@ def test_f32_output_from_bf16_and_fp8_pools(mla, ckv_dt, split):
     assert np.array_equal(host(lse16), host(lse32))
 
 
-def test_largest_split(mla):
+@pytest.mark.parametrize("ckv_dt", ["bf16", "fp8"])
+def test_largest_split(mla, ckv_dt):
     """A split of the largest supported size (1024 pages, 65536 tokens, every
-    page id held in LDS) followed by a short one, sampled rows against the
-    oracle."""
-    cfg = synth.small_config(B=1, H=16, T=1, seq_len=65536 + 100, seed=81)
+    page id held in LDS) followed by a short one, against the oracle."""
+    cfg = synth.small_config(B=1, H=16, T=1, seq_len=65536 + 100, seed=81, ckv_dt=ckv_dt)
     check_against_oracle(mla, synth.make_inputs(cfg), split_tokens=65536)
 
 
